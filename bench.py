@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention (forward + backward) on one MI355X.
+
+A step is one pass of the whole path -- fa_fwd then fa_bwd -- over the bf16
+GQA causal workload B=2, N=8192, Hq=32, Hkv=8, d=128 with synthetic inputs
+already resident in HBM.  Prints ONE JSON line (see --help).
+
+Algorithmic FLOP: forward 4*B*Hq*N^2*d halved for causal, backward 2.5x the
+forward (five products per visible score pair instead of two).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s at 1 GPU (bf16, d=128, N=8K causal); % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published figure
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample (whole heads are added until it is reached)")
+    return ap.parse_args()
+
+
+def visible_pairs(n, causal, window):
+    """Score pairs per (batch, head) by the counting convention of the metric:
+    N^2/2 for a causal mask, N^2 without one, the exact count for a window."""
+    wl, wr = window
+    if wl < 0 and wr < 0:
+        return n * n / 2 if causal else float(n * n)
+    total = 0
+    for i in range(n):
+        lo = 0 if wl < 0 else max(0, i - wl)
+        hi = i if causal else (n - 1 if wr < 0 else min(n - 1, i + wr))
+        if causal and wr >= 0:
+            hi = min(hi, i + wr)
+        total += max(0, hi - lo + 1)
+    return float(total)
+
+
+def flops(w):
+    fwd = 4.0 * w.batch * w.nheads_q * w.headdim * visible_pairs(w.seqlen, w.causal, w.window)
+    return fwd, 2.5 * fwd
+
+
+def cpu_baseline(w, q, k, v, do, budget_s):
+    """Time the float64 oracle on whole heads of the workload until budget_s is
+    reached (at least one head, at most one kv group); report TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    G = w.nheads_q // w.nheads_kv
+    kf = k[0:1, :, 0:1].double().numpy()
+    vf = v[0:1, :, 0:1].double().numpy()
+    done, t_total = 0, 0.0
+    for h in range(G):
+        qf = q[0:1, :, h:h + 1].double().numpy()
+        dof = do[0:1, :, h:h + 1].double().numpy()
+        t0 = time.perf_counter()
+        oracle.attention_fwd(qf, kf, vf, causal=w.causal, window=w.window)
+        oracle.attention_bwd(dof, qf, kf, vf, causal=w.causal, window=w.window)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    f_head = sum(flops(w)) / (w.batch * w.nheads_q)
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": f_head * done / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": blas_threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"{done} query head(s) x {w.seqlen} rows of batch 0 / kv head 0, fwd+bwd, float64 "
+                  f"NumPy oracle ({t_total:.1f} s; {len(os.sched_getaffinity(0))} cores in affinity mask, "
+                  f"CPU: {cpu_model})",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_07_amd as fa
+    from exact_tiled_attention_07_amd.workloads import BENCH_WORKLOAD, WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS[BENCH_WORKLOAD]
+    q_c, k_c, v_c, do_c = make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (q_c, k_c, v_c, do_c))
+    kw = dict(causal=w.causal, window_size=w.window)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.nheads_q, w.seqlen), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    params = fa.make_params(q, k, v, o, **kw)
+    ws = torch.empty(fa.bwd_workspace_size(params), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fwd(q, k, v, out=o, lse=lse, **kw)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.bwd(do, q, k, v, o, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in events]
+    step_ms = [e[0].elapsed_time(e[2]) for e in events]
+    assert torch.isfinite(o).all() and torch.isfinite(dq).all()
+
+    f_fwd, f_bwd = flops(w)
+    ms_per_step = wall * 1e3 / args.steps
+    value = (f_fwd + f_bwd) * args.steps / wall / 1e12
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    fwd_tflops = f_fwd / (fwd_avg * 1e-3) / 1e12
+    bwd_tflops = f_bwd / (bwd_avg * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q, k, v, dO; shapes of the pages' workloads)",
+        "config": {
+            "workload": w.name, "passes": "fwd+bwd", "batch": w.batch, "seqlen": w.seqlen,
+            "nheads_q": w.nheads_q, "nheads_kv": w.nheads_kv, "headdim": w.headdim,
+            "causal": w.causal, "window": list(w.window), "parallelism": "single GPU",
+        },
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(fwd_avg, 4),
+        "bwd_ms": round(bwd_avg, 4),
+        "fwd_tflops": round(fwd_tflops, 2),
+        "bwd_tflops": round(bwd_tflops, 2),
+        "event_ms_per_step": round(sum(step_ms) / len(step_ms), 4),
+        "roofline": {
+            "kernel": "fwd_mfma_kernel (fa_fwd, one launch per call)",
+            "bound": "mfma",
+            "achieved": round(fwd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q_c, k_c, v_c, do_c, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

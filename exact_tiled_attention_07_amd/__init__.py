@@ -1,0 +1,17 @@
+"""Exact tiled attention for AMD MI355X (gfx950).
+
+O = softmax(scale * Q K^T + causal/window mask) V, computed tile by tile with an
+online softmax in hand-written HIP kernels (32x32x16 MFMA for fp16/bf16, vector
+ALU for fp32), behind the C ABI of include/fa.h.  This package is the thin
+Python binding: torch provides device memory and streams only.
+
+    o, lse = fwd(q, k, v, causal=True)
+    dq, dk, dv = bwd(do, q, k, v, o, lse, causal=True)
+    o = attention(q, k, v, causal=True)          # autograd wrapper
+"""
+
+from ._native import (  # noqa: F401
+    FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_F16, FA_F32, FA_OK, SIGNATURES,
+    FaError, FaParams, attention, bwd, bwd_workspace_size, fwd, library_path, load_library,
+    make_params, version,
+)

@@ -1,0 +1,229 @@
+"""ctypes binding of libfa.so (the C ABI declared in include/fa.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the attention computation runs in the library's HIP
+kernels.  There is no CPU path: tensors must live on a GPU, and a missing
+library raises instead of falling back.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+_TORCH_DTYPE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+# Every function the header declares, with its ctypes signature.
+_I64x3 = ctypes.c_int64 * 3
+
+
+class FaParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seqlen_q", ctypes.c_int64),
+        ("seqlen_k", ctypes.c_int64),
+        ("nheads_q", ctypes.c_int64),
+        ("nheads_kv", ctypes.c_int64),
+        ("headdim", ctypes.c_int64),
+        ("q_strides", _I64x3),
+        ("k_strides", _I64x3),
+        ("v_strides", _I64x3),
+        ("o_strides", _I64x3),
+        ("dtype", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.POINTER(FaParams)
+_V = ctypes.c_void_p
+SIGNATURES = {
+    "fa_fwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
+    "fa_bwd_workspace_size": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
+    "fa_bwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fa_last_error": (ctypes.c_char_p, []),
+    "fa_version": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-OK fa_status returned by the library."""
+
+    def __init__(self, status, detail):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{_status_name(status)}: {detail}")
+
+
+def _status_name(status):
+    return {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_HIP"}.get(
+        status, f"status {status}")
+
+
+def library_path():
+    return LIB_PATH
+
+
+def load_library():
+    """Load libfa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m exact_tiled_attention_07_amd.build` "
+                "(there is no fallback implementation)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def version():
+    return load_library().fa_version()
+
+
+def _check(status):
+    if status != FA_OK:
+        lib = load_library()
+        raise FaError(status, lib.fa_last_error().decode(errors="replace"))
+
+
+def _strides3(t):
+    s = t.stride()
+    return _I64x3(s[0], s[1], s[2])
+
+
+def make_params(q, k, v, o, *, causal=False, window_size=(-1, -1), scale=None):
+    """FaParams for tensors shaped (batch, seqlen, nheads, headdim)."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D (batch, seqlen, nheads, headdim)")
+    if q.dtype not in _TORCH_DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for t in (k, v, o):
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v (and o) must share one dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    b, nq, hq, d = q.shape
+    if k.shape[0] != b or k.shape[3] != d or o.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v and o")
+    for t in (q, k, v, o):
+        if t.stride(3) != 1 and t.shape[3] > 1:
+            raise ValueError("the headdim axis must be contiguous (stride 1)")
+    wl, wr = window_size
+    p = FaParams()
+    p.batch, p.seqlen_q, p.seqlen_k = b, nq, k.shape[1]
+    p.nheads_q, p.nheads_kv, p.headdim = hq, k.shape[2], d
+    p.q_strides, p.k_strides = _strides3(q), _strides3(k)
+    p.v_strides, p.o_strides = _strides3(v), _strides3(o)
+    p.dtype = _TORCH_DTYPE[q.dtype]
+    p.scale = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    p.causal = 1 if causal else 0
+    p.window_left, p.window_right = int(wl), int(wr)
+    return p
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU (there is no CPU path)")
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(None)
+
+
+def fwd(q, k, v, *, causal=False, window_size=(-1, -1), scale=None, out=None, lse=None):
+    """Exact attention forward: returns (o, lse).
+
+    q (B, Nq, Hq, d); k, v (B, Nk, Hkv, d); o like q; lse float32 (B, Hq, Nq).
+    """
+    _require_gpu(q, k, v)
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    p = make_params(q, k, v, out, causal=causal, window_size=window_size, scale=scale)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q.device)))
+    return out, lse
+
+
+def bwd_workspace_size(params):
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.fa_bwd_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return n.value
+
+
+def bwd(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1), scale=None,
+        dq=None, dk=None, dv=None, workspace=None):
+    """Exact attention backward: returns (dq, dk, dv) of L = sum(out * dout).
+
+    dout uses out's layout; dq gets q's strides, dk/dv get k's and v's.
+    """
+    _require_gpu(dout, q, k, v, out, lse)
+    lib = load_library()
+    if dout.shape != q.shape or dout.dtype != q.dtype or dout.stride() != out.stride():
+        raise ValueError("dout must have the shape, dtype and strides of out")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[0], q.shape[2], q.shape[1]) \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (batch, nheads_q, seqlen_q) tensor")
+    p = make_params(q, k, v, out, causal=causal, window_size=window_size, scale=scale)
+    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device) if dv is None else dv
+    for g, ref in ((dq, q), (dk, k), (dv, v)):
+        if g.shape != ref.shape or g.stride() != ref.stride() or g.dtype != ref.dtype:
+            raise ValueError("gradient buffers must match the shape, strides and dtype of q/k/v")
+    need = bwd_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd(ctypes.byref(p), _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                          _stream(q.device)))
+    return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal, window_size, scale):
+        o, lse = fwd(q, k, v, causal=causal, window_size=window_size, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.cfg = (causal, window_size, scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        causal, window_size, scale = ctx.cfg
+        do = do.contiguous() if do.stride() != o.stride() else do
+        if do.stride() != o.stride():
+            do = torch.empty_strided(o.shape, o.stride(), dtype=o.dtype, device=o.device).copy_(do)
+        dq, dk, dv = bwd(do, q, k, v, o, lse, causal=causal, window_size=window_size, scale=scale)
+        return dq, dk, dv, None, None, None
+
+
+def attention(q, k, v, *, causal=False, window_size=(-1, -1), scale=None):
+    """Differentiable exact attention over (batch, seqlen, nheads, headdim) tensors."""
+    return _Attention.apply(q, k, v, causal, tuple(window_size), scale)

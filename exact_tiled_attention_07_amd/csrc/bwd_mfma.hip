@@ -1,0 +1,460 @@
+// Backward attention for fp16/bf16 on gfx950 with 32x32x16 MFMA.
+//
+// The backward pass does not keep the attention matrix: it recomputes each
+// probability tile from Q, K and the forward log-sum-exp when it is needed
+// ([P4] "FlashAttention 实战指南", section "长序列注意力为什么会爆内存",
+// recomputation traded for memory).  The gradient formulas are the exact
+// derivative of the forward:
+//   P = exp(scale*QK^T - LSE),  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
+//   dS = P * (dP - D),  dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
+//
+// Three kernels, none with atomics (results are bitwise repeatable):
+//   preprocess  D_i for every query row (fp32 workspace)
+//   dK/dV       one workgroup per (batch, kv head, tile of 32*NW keys); each
+//               wave keeps its 32 keys' K and V in registers and its dK^T, dV^T
+//               accumulators in registers, loops over the query heads of the
+//               group and the visible query tiles:
+//                 S  = Q K^T        (A = Q rows in LDS, B = K registers)
+//                 dV^T += dO^T P    (A = dO^T transposed in LDS, B = P)
+//                 dP = dO V^T       (A = dO rows in LDS, B = V registers)
+//                 dK^T += Q^T dS    (A = Q^T transposed in LDS, B = dS)
+//               GQA sums over the group inside the workgroup.
+//   dQ          one workgroup per (batch, query head, tile of 32*NW queries);
+//               the forward's layout (one query per lane):
+//                 S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T
+// The dQ kernel recomputes S and dP (7 tile products per score pair instead of
+// 5) in exchange for no atomic accumulation and no dQ workspace.
+#include "common.hpp"
+#include "launch.hpp"
+#include "tile_io.hpp"
+
+namespace fa {
+
+// ---------------------------------------------------------------------------
+// D_i = sum_c dout[i, c] * o[i, c]   (any dtype; 16 lanes per row)
+// ---------------------------------------------------------------------------
+template <int ELT>  // element bytes: 4 (fp32) or 2 (fp16/bf16)
+__global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a) {
+  constexpr int EPC = 16 / ELT;  // elements per 16-byte chunk
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const int64_t rows = (int64_t)a.B * a.Nq * a.Hq;
+  float acc = 0.f;
+  int h = 0, i = 0, b = 0;
+  if (row < rows) {
+    h = (int)(row % a.Hq);
+    const int64_t t = row / a.Hq;
+    i = (int)(t % a.Nq);
+    b = (int)(t / a.Nq);
+    const char* dop = static_cast<const char*>(a.dout) +
+                      (b * a.o_sb + (int64_t)i * a.o_sn + h * a.o_sh) * ELT;
+    const char* op = static_cast<const char*>(a.o) + (b * a.o_sb + (int64_t)i * a.o_sn + h * a.o_sh) * ELT;
+    for (int cc = sub; cc * EPC < a.D; cc += 16) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(dop + cc * 16);
+      const u32x4 y = *reinterpret_cast<const u32x4*>(op + cc * 16);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (ELT == 4) {
+          acc = fmaf(__uint_as_float(x[w]), __uint_as_float(y[w]), acc);
+        } else if (a.dtype == kBF16) {
+          acc = fmaf(BF16::to_f32(x[w] & 0xffffu), BF16::to_f32(y[w] & 0xffffu), acc);
+          acc = fmaf(BF16::to_f32(x[w] >> 16), BF16::to_f32(y[w] >> 16), acc);
+        } else {
+          acc = fmaf(F16::to_f32(x[w] & 0xffffu), F16::to_f32(y[w] & 0xffffu), acc);
+          acc = fmaf(F16::to_f32(x[w] >> 16), F16::to_f32(y[w] >> 16), acc);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (row < rows && sub == 0) a.dsum[((int64_t)b * a.Hq + h) * a.Nq + i] = acc;
+}
+
+hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.Nq * a.Hq;
+  if (rows == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((rows + 15) / 16);
+  if (a.dtype == kF32)
+    hipLaunchKernelGGL(bwd_preprocess_kernel<4>, dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(bwd_preprocess_kernel<2>, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// log2-domain LSE of a query row; a row that sees no key (LSE = -inf) gets +inf
+// so that every recomputed probability exp2(s*c - lse2) of it is exactly 0.
+__device__ __forceinline__ float lse_log2(float lse) {
+  return (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV
+// ---------------------------------------------------------------------------
+template <class T, int D, int BMQ, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(AttnArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int BNK = NW * 32;  // keys per workgroup
+  using Tile = TileRegs<D, BMQ, NT>;
+  constexpr int RP = RowPitch<D>::value;
+  constexpr int CP = ColPitch<BMQ, Tile::R>::value;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[BMQ * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[BMQ * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * CP];
+  __shared__ __attribute__((aligned(16))) uint16_t dOt[D * CP];
+  __shared__ __attribute__((aligned(16))) float lse2s[BMQ];
+  __shared__ __attribute__((aligned(16))) float dsums[BMQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int n_kt = (a.Nk + BNK - 1) / BNK;
+  // Under a causal mask the first key tiles see the most queries: run them first.
+  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_kt, 1, false, a.xcd_remap);
+  const int b = it.unit / a.Hkv, hk = it.unit % a.Hkv;
+  const int k0 = it.tile * BNK;
+  const int key = k0 + wave * 32 + l32;  // this lane's key (accumulator column)
+
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + hk * a.v_sh;
+
+  // K and V as B operands (lane: key, d = 16*st + 8*hf + 0..7).
+  u32x4 kf[D / 16], vf[D / 16];
+  if (key < a.Nk) {
+    const uint16_t* kr = Kp + (int64_t)key * a.k_sn + 8 * hf;
+    const uint16_t* vr = Vp + (int64_t)key * a.v_sn + 8 * hf;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      kf[st] = *reinterpret_cast<const u32x4*>(kr + 16 * st);
+      vf[st] = *reinterpret_cast<const u32x4*>(vr + 16 * st);
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) kf[st] = vf[st] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dka[db] = dva[db] = f32x16{};
+
+  const int k_last = min(k0 + BNK, a.Nk) - 1;
+  const int i_lo = query_lo(a, k0), i_hi = query_hi(a, k_last);
+  const int qt_lo = i_lo / BMQ;
+  const int qt_hi = (i_hi >= i_lo) ? i_hi / BMQ : qt_lo - 1;
+  const float c = a.scale_log2;
+
+  for (int g = 0; g < a.G; ++g) {
+    const int hq = hk * a.G + g;
+    const uint16_t* Qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh;
+    const uint16_t* dOp = static_cast<const uint16_t*>(a.dout) + b * a.o_sb + hq * a.o_sh;
+    const float* lsep = a.lse + ((int64_t)b * a.Hq + hq) * a.Nq;
+    const float* dsp = a.dsum + ((int64_t)b * a.Hq + hq) * a.Nq;
+
+    Tile qt, dt;
+    if (qt_lo <= qt_hi) {
+      qt.load(Qp, a.q_sn, qt_lo * BMQ, a.Nq, tid);
+      dt.load(dOp, a.o_sn, qt_lo * BMQ, a.Nq, tid);
+    }
+    for (int t = qt_lo; t <= qt_hi; ++t) {
+      const int i0 = t * BMQ;
+      __syncthreads();
+      qt.template store_rows<RP>(Qs, tid);
+      qt.template store_cols<CP>(Qt, tid);
+      dt.template store_rows<RP>(dOs, tid);
+      dt.template store_cols<CP>(dOt, tid);
+      if (tid < BMQ) {
+        const int i = i0 + tid;
+        lse2s[tid] = (i < a.Nq) ? lse_log2(lsep[i]) : INFINITY;
+        dsums[tid] = (i < a.Nq) ? dsp[i] : 0.f;
+      }
+      __syncthreads();
+      if (t < qt_hi) {
+        qt.load(Qp, a.q_sn, i0 + BMQ, a.Nq, tid);
+        dt.load(dOp, a.o_sn, i0 + BMQ, a.Nq, tid);
+      }
+
+      // S = Q K^T; s[qb][r] is query i0 + 32*qb + 8*(r/4) + 4*hf + r%4.
+      f32x16 s[BMQ / 32];
+#pragma unroll
+      for (int qb = 0; qb < BMQ / 32; ++qb) s[qb] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+        for (int qb = 0; qb < BMQ / 32; ++qb)
+          s[qb] = T::mfma(lds_row8(Qs + (32 * qb + l32) * RP + 16 * st + 8 * hf), kf[st], s[qb]);
+      }
+      // Mask: exact per-element test only where the tile pair is not fully visible.
+      const int i_end = min(i0 + BMQ, a.Nq) - 1;
+      const bool full = (key_lo(a, i_end) <= k0) && (key_hi(a, i0) >= k_last);
+      if (!full) {
+#pragma unroll
+        for (int qb = 0; qb < BMQ / 32; ++qb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = i0 + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key < key_lo(a, i) || key > key_hi(a, i)) s[qb][r] = -INFINITY;
+          }
+        }
+      }
+      // P = exp2(s*c - lse2) and dV^T += dO^T P.
+      u32x4 pf[BMQ / 16];
+      float p[BMQ / 32][16];
+#pragma unroll
+      for (int qb = 0; qb < BMQ / 32; ++qb) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 32 * qb + 8 * g4 + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[qb][4 * g4 + e] = fast_exp2(fmaf(s[qb][4 * g4 + e], c, -l4[e]));
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const float* pp = &p[qb][8 * tt];
+          pf[2 * qb + tt] = u32x4{T::pack(pp[0], pp[1]), T::pack(pp[2], pp[3]), T::pack(pp[4], pp[5]),
+                                  T::pack(pp[6], pp[7])};
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int si = 0; si < BMQ / 16; ++si)
+          dva[db] = T::mfma(lds_col8(dOt + (32 * db + l32) * CP + 16 * si + 4 * hf), pf[si], dva[db]);
+      }
+      // dP = dO V^T.
+      f32x16 dp[BMQ / 32];
+#pragma unroll
+      for (int qb = 0; qb < BMQ / 32; ++qb) dp[qb] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+        for (int qb = 0; qb < BMQ / 32; ++qb)
+          dp[qb] = T::mfma(lds_row8(dOs + (32 * qb + l32) * RP + 16 * st + 8 * hf), vf[st], dp[qb]);
+      }
+      // dS = P * (dP - D) and dK^T += Q^T dS.
+      u32x4 dsf[BMQ / 16];
+#pragma unroll
+      for (int qb = 0; qb < BMQ / 32; ++qb) {
+        float ds[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsums + 32 * qb + 8 * g4 + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[4 * g4 + e] = p[qb][4 * g4 + e] * (dp[qb][4 * g4 + e] - d4[e]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const float* q8 = &ds[8 * tt];
+          dsf[2 * qb + tt] = u32x4{T::pack(q8[0], q8[1]), T::pack(q8[2], q8[3]), T::pack(q8[4], q8[5]),
+                                   T::pack(q8[6], q8[7])};
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int si = 0; si < BMQ / 16; ++si)
+          dka[db] = T::mfma(lds_col8(Qt + (32 * db + l32) * CP + 16 * si + 4 * hf), dsf[si], dka[db]);
+      }
+    }
+  }
+
+  // Store dK = scale * dK^T^T and dV: lane holds d rows 32*db + 8*g4 + 4*hf + 0..3.
+  if (key < a.Nk) {
+    uint16_t* dkp = static_cast<uint16_t*>(a.dk) + b * a.k_sb + hk * a.k_sh + (int64_t)key * a.k_sn;
+    uint16_t* dvp = static_cast<uint16_t*>(a.dv) + b * a.v_sb + hk * a.v_sh + (int64_t)key * a.v_sn;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * hf;
+        *reinterpret_cast<u32x2*>(dkp + d0) =
+            u32x2{T::pack(dka[db][4 * g4] * sc, dka[db][4 * g4 + 1] * sc),
+                  T::pack(dka[db][4 * g4 + 2] * sc, dka[db][4 * g4 + 3] * sc)};
+        *reinterpret_cast<u32x2*>(dvp + d0) =
+            u32x2{T::pack(dva[db][4 * g4], dva[db][4 * g4 + 1]), T::pack(dva[db][4 * g4 + 2], dva[db][4 * g4 + 3])};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+template <class T, int D, int BN, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int BM = NW * 32;
+  using Tile = TileRegs<D, BN, NT>;
+  constexpr int RP = RowPitch<D>::value;
+  constexpr int CP = ColPitch<BN, Tile::R>::value;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * RP];
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * CP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int n_qt = (a.Nq + BM - 1) / BM;
+  const bool heavy_last = (a.causal || a.wr >= 0) && a.wl < 0;
+  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_qt, a.G, heavy_last, a.xcd_remap);
+  const int b = it.unit / a.Hkv, hk = it.unit % a.Hkv;
+  const int hq = hk * a.G + it.sub;
+  const int q0 = it.tile * BM;
+  const int qrow = q0 + wave * 32 + l32;
+
+  const uint16_t* Qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh;
+  const uint16_t* dOp = static_cast<const uint16_t*>(a.dout) + b * a.o_sb + hq * a.o_sh;
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + hk * a.v_sh;
+
+  u32x4 qf[D / 16], df[D / 16];
+  float lse2 = INFINITY, dsum = 0.f;
+  if (qrow < a.Nq) {
+    const uint16_t* qr = Qp + (int64_t)qrow * a.q_sn + 8 * hf;
+    const uint16_t* dr = dOp + (int64_t)qrow * a.o_sn + 8 * hf;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      qf[st] = *reinterpret_cast<const u32x4*>(qr + 16 * st);
+      df[st] = *reinterpret_cast<const u32x4*>(dr + 16 * st);
+    }
+    const int64_t ri = ((int64_t)b * a.Hq + hq) * a.Nq + qrow;
+    lse2 = lse_log2(a.lse[ri]);
+    dsum = a.dsum[ri];
+  } else {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) qf[st] = df[st] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const int lo_i = key_lo(a, qrow), hi_i = key_hi(a, qrow);
+  const int q_last = min(q0 + BM, a.Nq) - 1;
+  const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
+  const int lo_max = key_lo(a, q_last), hi_min = key_hi(a, q0);
+  const int t_lo = kv_lo / BN;
+  const int t_hi = (kv_hi >= kv_lo) ? kv_hi / BN : t_lo - 1;
+  const float c = a.scale_log2;
+
+  f32x16 dqa[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dqa[db] = f32x16{};
+
+  Tile kt, vt;
+  if (t_lo <= t_hi) {
+    kt.load(Kp, a.k_sn, t_lo * BN, a.Nk, tid);
+    vt.load(Vp, a.v_sn, t_lo * BN, a.Nk, tid);
+  }
+  for (int t = t_lo; t <= t_hi; ++t) {
+    const int j0 = t * BN;
+    __syncthreads();
+    kt.template store_rows<RP>(Ks, tid);
+    kt.template store_cols<CP>(Kt, tid);
+    vt.template store_rows<RP>(Vs, tid);
+    __syncthreads();
+    if (t < t_hi) {
+      kt.load(Kp, a.k_sn, j0 + BN, a.Nk, tid);
+      vt.load(Vp, a.v_sn, j0 + BN, a.Nk, tid);
+    }
+    // S^T = K Q^T and dP^T = V dO^T; element [kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
+    f32x16 s[BN / 32], dp[BN / 32];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) s[kb] = dp[kb] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        s[kb] = T::mfma(lds_row8(Ks + (32 * kb + l32) * RP + 16 * st + 8 * hf), qf[st], s[kb]);
+        dp[kb] = T::mfma(lds_row8(Vs + (32 * kb + l32) * RP + 16 * st + 8 * hf), df[st], dp[kb]);
+      }
+    }
+    const bool full = (j0 >= lo_max) && (j0 + BN - 1 <= hi_min);
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key < lo_i || key > hi_i) s[kb][r] = -INFINITY;
+        }
+      }
+    }
+    // dS^T = P^T * (dP^T - D) as B operands, then dQ^T += K^T dS^T.
+    u32x4 dsf[BN / 16];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * tt + e;
+          const float pr = fast_exp2(fmaf(s[kb][r], c, -lse2));
+          ds[e] = pr * (dp[kb][r] - dsum);
+        }
+        dsf[2 * kb + tt] = u32x4{T::pack(ds[0], ds[1]), T::pack(ds[2], ds[3]), T::pack(ds[4], ds[5]),
+                                 T::pack(ds[6], ds[7])};
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int si = 0; si < BN / 16; ++si)
+        dqa[db] = T::mfma(lds_col8(Kt + (32 * db + l32) * CP + 16 * si + 4 * hf), dsf[si], dqa[db]);
+    }
+  }
+
+  if (qrow < a.Nq) {
+    uint16_t* dqp = static_cast<uint16_t*>(a.dq) + b * a.q_sb + hq * a.q_sh + (int64_t)qrow * a.q_sn;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * hf;
+        *reinterpret_cast<u32x2*>(dqp + d0) =
+            u32x2{T::pack(dqa[db][4 * g4] * sc, dqa[db][4 * g4 + 1] * sc),
+                  T::pack(dqa[db][4 * g4 + 2] * sc, dqa[db][4 * g4 + 3] * sc)};
+      }
+    }
+  }
+}
+
+template <class T, int D>
+static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream) {
+  constexpr int NW = 4;
+  constexpr int BMQ = 64;        // queries per dK/dV iteration
+  constexpr int BN_DQ = 64;      // keys per dQ iteration
+  hipError_t e = launch_bwd_preprocess(a, stream);
+  if (e != hipSuccess) return e;
+  AttnArgs args = a;
+  args.xcd_remap = a.xcd_remap && ((a.B * a.Hkv) % 8 == 0);
+  const int n_kt = (a.Nk + NW * 32 - 1) / (NW * 32);
+  const int64_t grid_kv = (int64_t)a.B * a.Hkv * n_kt;
+  if (grid_kv > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, BMQ, NW>), dim3((unsigned)grid_kv), dim3(NW * 64), 0,
+                       stream, args);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int n_qt = (a.Nq + NW * 32 - 1) / (NW * 32);
+  const int64_t grid_q = (int64_t)a.B * a.Hkv * n_qt * a.G;
+  if (grid_q > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, BN_DQ, NW>), dim3((unsigned)grid_q), dim3(NW * 64), 0,
+                       stream, args);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t stream) {
+  if (a.dtype == kBF16) {
+    if (a.D == 128) return launch_bwd_t<BF16, 128>(a, stream);
+    if (a.D == 64) return launch_bwd_t<BF16, 64>(a, stream);
+  } else if (a.dtype == kF16) {
+    if (a.D == 128) return launch_bwd_t<F16, 128>(a, stream);
+    if (a.D == 64) return launch_bwd_t<F16, 64>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

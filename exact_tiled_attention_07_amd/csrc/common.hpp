@@ -1,0 +1,165 @@
+// Shared definitions for the gfx950 attention kernels: the launch argument
+// block, element-type traits, the 32x32x16 MFMA wrappers and the mask rule.
+//
+// Mask rule ([P4] "FlashAttention 实战指南", section "进阶参数如何配置causal、
+// window_size 与 MQA/GQA", and section "上手 FlashAttention 的三步走" for causal):
+// with i' = i + (seqlen_k - seqlen_q), key j is visible from query i iff
+// j < seqlen_k, (!causal || j <= i'), (left < 0 || j >= i' - left) and
+// (right < 0 || j <= i' + right).  Every kernel reduces this to a per-query
+// closed interval [key_lo(i), key_hi(i)].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+enum DType : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Everything a launch needs; filled and validated by the C ABI layer.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;        // (B, Hq, Nq) natural log
+  const void* dout;  // backward only
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;       // (B, Hq, Nq) workspace: D_i = sum_c dout*o
+  int64_t q_sb, q_sn, q_sh;
+  int64_t k_sb, k_sn, k_sh;
+  int64_t v_sb, v_sn, v_sh;
+  int64_t o_sb, o_sn, o_sh;
+  int32_t B, Nq, Nk, Hq, Hkv, G, D;
+  int32_t dtype;
+  float scale;       // multiplies q.k
+  float scale_log2;  // scale * log2(e): exp(scale*x) == exp2(scale_log2*x)
+  int32_t causal, wl, wr;  // wl/wr: -1 = unbounded
+  int32_t delta;     // Nk - Nq (queries aligned to the end of the keys)
+  int32_t xcd_remap; // 1: map consecutive workgroup ids onto one XCD's work
+};
+
+static constexpr float kLog2e = 1.4426950408889634f;
+static constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Mask interval for one query row (i' = i + delta).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int key_lo(const AttnArgs& a, int i) {
+  int lo = 0;
+  if (a.wl >= 0) lo = max(lo, i + a.delta - a.wl);
+  return lo;
+}
+__device__ __forceinline__ int key_hi(const AttnArgs& a, int i) {
+  int hi = a.Nk - 1;
+  if (a.causal) hi = min(hi, i + a.delta);
+  if (a.wr >= 0) hi = min(hi, i + a.delta + a.wr);
+  return hi;
+}
+// Range of queries that see at least one key of [k0, k1] (inclusive).
+__device__ __forceinline__ int query_lo(const AttnArgs& a, int k0) {
+  int lo = 0;
+  if (a.causal) lo = max(lo, k0 - a.delta);
+  if (a.wr >= 0) lo = max(lo, k0 - a.delta - a.wr);
+  return lo;
+}
+__device__ __forceinline__ int query_hi(const AttnArgs& a, int k1) {
+  int hi = a.Nq - 1;
+  if (a.wl >= 0) hi = min(hi, k1 - a.delta + a.wl);
+  return hi;
+}
+
+// ---------------------------------------------------------------------------
+// Element types.  Raw 16-bit storage is uint16_t; MFMA operands are 8
+// elements (16 bytes) per lane, carried as u32x4.
+// ---------------------------------------------------------------------------
+struct BF16 {
+  static constexpr int kId = kBF16;
+  __device__ __forceinline__ static f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static float to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+  }
+  // Two floats -> packed pair (lo in bits 0..15), round to nearest even.
+  __device__ __forceinline__ static uint32_t pack(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+  }
+};
+
+struct F16 {
+  static constexpr int kId = kF16;
+  __device__ __forceinline__ static f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static float to_f32(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+  }
+  __device__ __forceinline__ static uint32_t pack(float lo, float hi) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 r;
+    r[0] = (_Float16)lo;
+    r[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of the lane 32 positions away (lanes l and l^32 of a wave64).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// ---------------------------------------------------------------------------
+// Workgroup -> work-item decode.  On MI355X consecutive workgroup ids are
+// dispatched round-robin over the 8 XCDs, each with its own L2.  With
+// xcd_remap, id w runs on XCD w % 8, and the work of that XCD is a contiguous
+// range of "units" (here (batch, kv head) pairs) so that the workgroups
+// sharing K/V also share an L2.  Inside an XCD the order is tile-major with
+// the heaviest tiles (largest causal prefix) first.
+// ---------------------------------------------------------------------------
+struct WorkItem {
+  int unit;   // (batch * Hkv + kv head)
+  int tile;   // tile index along the sequence
+  int sub;    // index inside the unit's group (query head offset)
+};
+
+__device__ __forceinline__ WorkItem decode_work(int w, int n_units, int n_tiles, int n_sub,
+                                                bool heavy_last_first, bool xcd_remap) {
+  WorkItem it;
+  int slot, ui, per;
+  if (xcd_remap) {
+    const int xcd = w & 7;
+    slot = w >> 3;
+    per = n_units >> 3;  // units per XCD (host guarantees n_units % 8 == 0)
+    it.sub = slot % n_sub;
+    const int t = slot / n_sub;
+    ui = t % per;
+    const int tr = t / per;
+    it.unit = xcd * per + ui;
+    it.tile = heavy_last_first ? (n_tiles - 1 - tr) : tr;
+  } else {
+    it.sub = w % n_sub;
+    const int t = w / n_sub;
+    it.unit = t % n_units;
+    const int tr = t / n_units;
+    it.tile = heavy_last_first ? (n_tiles - 1 - tr) : tr;
+  }
+  return it;
+}
+
+}  // namespace fa

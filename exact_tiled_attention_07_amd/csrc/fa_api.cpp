@@ -1,0 +1,238 @@
+// C ABI of the attention library (declared in include/fa.h): argument
+// validation, device capability check and dispatch to the HIP launchers.
+//
+// Every argument is checked on the host before the first HIP call, so an
+// invalid call returns its status without touching the device.  No C++
+// exception crosses the boundary.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status fail(fa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+size_t elem_bytes(fa_dtype d) { return d == FA_F32 ? 4 : 2; }
+
+constexpr int64_t kMaxSeq = int64_t(1) << 30;
+constexpr int64_t kMaxHeads = int64_t(1) << 16;
+constexpr int64_t kMaxBatch = int64_t(1) << 20;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+fa_status check_params(const fa_params* p) {
+  if (!p) return fail(FA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 0 || p->seqlen_q < 0 || p->seqlen_k < 0)
+    return fail(FA_ERR_INVALID_ARG, "batch/seqlen must be >= 0 (got %lld, %lld, %lld)",
+                (long long)p->batch, (long long)p->seqlen_q, (long long)p->seqlen_k);
+  if (p->nheads_q < 1 || p->nheads_kv < 1 || p->headdim < 1)
+    return fail(FA_ERR_INVALID_ARG, "nheads_q, nheads_kv and headdim must be >= 1");
+  if (p->nheads_q % p->nheads_kv != 0)
+    return fail(FA_ERR_INVALID_ARG, "nheads_q (%lld) must be a multiple of nheads_kv (%lld)",
+                (long long)p->nheads_q, (long long)p->nheads_kv);
+  if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16)
+    return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)p->dtype);
+  if (!(std::isfinite(p->scale) && p->scale > 0.f))
+    return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (p->causal != 0 && p->causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->window_left < -1 || p->window_right < -1)
+    return fail(FA_ERR_INVALID_ARG, "window bounds must be >= -1 (got %d, %d)", p->window_left,
+                p->window_right);
+  if (p->seqlen_q > kMaxSeq || p->seqlen_k > kMaxSeq || p->nheads_q > kMaxHeads || p->batch > kMaxBatch)
+    return fail(FA_ERR_UNSUPPORTED, "sizes exceed this build's limits");
+  if (p->batch * p->nheads_q * ((p->seqlen_q + 31) / 32) >= (int64_t(1) << 31) ||
+      p->batch * p->nheads_kv * ((p->seqlen_k + 31) / 32) >= (int64_t(1) << 31))
+    return fail(FA_ERR_UNSUPPORTED, "launch grid would exceed 2^31 workgroups");
+  if (p->dtype == FA_F32) {
+    if (p->headdim > 128 || p->headdim % 4 != 0)
+      return fail(FA_ERR_UNSUPPORTED, "fp32 headdim must be a multiple of 4 in [4, 128] (got %lld)",
+                  (long long)p->headdim);
+  } else if (p->headdim != 64 && p->headdim != 128) {
+    return fail(FA_ERR_UNSUPPORTED, "fp16/bf16 headdim must be 64 or 128 (got %lld)", (long long)p->headdim);
+  }
+  const int64_t* strides[4] = {p->q_strides, p->k_strides, p->v_strides, p->o_strides};
+  const char* names[4] = {"q", "k", "v", "o"};
+  const int64_t eb = (int64_t)elem_bytes(p->dtype);
+  for (int t = 0; t < 4; ++t) {
+    for (int i = 0; i < 3; ++i) {
+      const int64_t s = strides[t][i];
+      if (s < 0) return fail(FA_ERR_UNSUPPORTED, "%s_strides[%d] is negative", names[t], i);
+      if ((s * eb) % 16 != 0)
+        return fail(FA_ERR_UNSUPPORTED, "%s_strides[%d]=%lld is not a multiple of 16 bytes", names[t], i,
+                    (long long)s);
+    }
+  }
+  return FA_OK;
+}
+
+bool empty_problem(const fa_params* p) { return p->batch == 0 || p->seqlen_q == 0; }
+
+fa_status check_ptr(const void* ptr, const char* name, bool nonempty) {
+  if (!nonempty) return FA_OK;
+  if (!ptr) return fail(FA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(FA_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+  return FA_OK;
+}
+
+// Per-device "is this a gfx950" cache (hipGetDeviceProperties is slow).
+constexpr int kMaxDevices = 64;
+int g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+std::mutex g_arch_mu;
+
+fa_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_arch_mu);
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_arch_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    if (g_arch_ok[dev] < 0)
+      return fail(FA_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+  }
+  if (g_arch_ok[dev] < 0) return fail(FA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return FA_OK;
+}
+
+fa::AttnArgs make_args(const fa_params* p) {
+  fa::AttnArgs a{};
+  a.q_sb = p->q_strides[0]; a.q_sn = p->q_strides[1]; a.q_sh = p->q_strides[2];
+  a.k_sb = p->k_strides[0]; a.k_sn = p->k_strides[1]; a.k_sh = p->k_strides[2];
+  a.v_sb = p->v_strides[0]; a.v_sn = p->v_strides[1]; a.v_sh = p->v_strides[2];
+  a.o_sb = p->o_strides[0]; a.o_sn = p->o_strides[1]; a.o_sh = p->o_strides[2];
+  a.B = (int32_t)p->batch;
+  a.Nq = (int32_t)p->seqlen_q;
+  a.Nk = (int32_t)p->seqlen_k;
+  a.Hq = (int32_t)p->nheads_q;
+  a.Hkv = (int32_t)p->nheads_kv;
+  a.G = (int32_t)(p->nheads_q / p->nheads_kv);
+  a.D = (int32_t)p->headdim;
+  a.dtype = p->dtype == FA_F32 ? fa::kF32 : (p->dtype == FA_F16 ? fa::kF16 : fa::kBF16);
+  a.scale = p->scale;
+  a.scale_log2 = p->scale * fa::kLog2e;
+  a.causal = p->causal;
+  a.wl = p->window_left;
+  a.wr = p->window_right;
+  a.delta = (int32_t)(p->seqlen_k - p->seqlen_q);
+  a.xcd_remap = 1;
+  return a;
+}
+
+size_t workspace_bytes_for(const fa_params* p) {
+  const size_t n = (size_t)p->batch * (size_t)p->nheads_q * (size_t)p->seqlen_q * sizeof(float);
+  return ((n + 255) / 256) * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const fa_params* params, const void* q, const void* k, const void* v, void* o, float* lse,
+                 void* stream) {
+  fa_status s = check_params(params);
+  if (s != FA_OK) return s;
+  const bool nonempty = !empty_problem(params);
+  const bool kv_nonempty = nonempty && params->seqlen_k > 0;  // K/V are read only if there are queries
+  if ((s = check_ptr(q, "q", nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(k, "k", kv_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(v, "v", kv_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(o, "o", nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(lse, "lse", nonempty)) != FA_OK) return s;
+  if (nonempty && (o == q || o == k || o == v)) return fail(FA_ERR_INVALID_ARG, "o must not alias q, k or v");
+  if (!nonempty) return FA_OK;
+  if ((s = check_device()) != FA_OK) return s;
+  fa::AttnArgs a = make_args(params);
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = (params->dtype == FA_F32) ? fa::launch_fwd_f32(a, st) : fa::launch_fwd_mfma(a, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+fa_status fa_bwd_workspace_size(const fa_params* params, size_t* bytes) {
+  fa_status s = check_params(params);
+  if (s != FA_OK) return s;
+  if (!bytes) return fail(FA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = workspace_bytes_for(params);
+  return FA_OK;
+}
+
+fa_status fa_bwd(const fa_params* params, const void* dout, const void* q, const void* k, const void* v,
+                 const void* o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  fa_status s = check_params(params);
+  if (s != FA_OK) return s;
+  const bool q_nonempty = !empty_problem(params);
+  const bool kv_nonempty = params->batch > 0 && params->seqlen_k > 0;
+  if ((s = check_ptr(dout, "dout", q_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(q, "q", q_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(k, "k", kv_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(v, "v", kv_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(o, "o", q_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(lse, "lse", q_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(dq, "dq", q_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(dk, "dk", kv_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(dv, "dv", kv_nonempty)) != FA_OK) return s;
+  const size_t need = workspace_bytes_for(params);
+  if (need > 0) {
+    if ((s = check_ptr(workspace, "workspace", true)) != FA_OK) return s;
+    if (workspace_bytes < need)
+      return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  }
+  if (q_nonempty || kv_nonempty) {
+    const void* outs[3] = {dq, dk, dv};
+    const void* ins[6] = {dout, q, k, v, o, lse};
+    for (const void* x : outs)
+      for (const void* y : ins)
+        if (x && x == y) return fail(FA_ERR_INVALID_ARG, "gradient outputs must not alias the inputs");
+  }
+  if (!q_nonempty && !kv_nonempty) return FA_OK;
+  if ((s = check_device()) != FA_OK) return s;
+  fa::AttnArgs a = make_args(params);
+  a.q = q; a.k = k; a.v = v; a.o = const_cast<void*>(o); a.lse = const_cast<float*>(lse);
+  a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dsum = static_cast<float*>(workspace);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = (params->dtype == FA_F32) ? fa::launch_bwd_f32(a, st) : fa::launch_bwd_mfma(a, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+const char* fa_status_string(fa_status status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+  }
+  return "FA_STATUS_UNKNOWN";
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+int fa_version(void) { return FA_VERSION; }
+
+}  // extern "C"

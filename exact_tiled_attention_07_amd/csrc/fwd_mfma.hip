@@ -1,0 +1,212 @@
+// Forward attention for fp16/bf16 on gfx950 with 32x32x16 MFMA.
+//
+// The method ([P4] "FlashAttention 实战指南", section "长序列注意力为什么会爆内存"):
+// Q, K and V are cut into tiles; one tile of queries stays on chip while K/V
+// tiles stream through LDS; each K/V tile's scores and softmax are computed on
+// chip, and an online softmax keeps the running row maximum and row sum so
+// that the full score matrix never exists.  The output is the exact attention
+// result; the kernel also writes the per-row log-sum-exp for the backward pass.
+//
+// gfx950 mapping.  One workgroup = NW waves = a tile of BM = 32*NW queries of
+// one (batch, query head); each wave owns 32 query rows.  For every K/V tile of
+// BN keys:
+//   S^T (BN x 32) = K Q^T      A operand = K rows from LDS, B = Q (registers)
+//   online softmax             lane l holds query l%32 and 16 keys per 32x32
+//                              block, so row max/sum are in-register plus one
+//                              exchange with lane l^32
+//   O^T (D x 32) += V^T P^T    A operand = V^T from a transposed LDS copy,
+//                              B = P^T straight from the softmax registers
+// The O rescale by exp(m_old - m_new) is a per-lane scalar (one query per lane).
+// Scores are kept in raw units; exp(scale*(s - m)) is evaluated as
+// exp2(s*c - m*c) with c = scale*log2(e), one FMA and one v_exp_f32.
+#include "common.hpp"
+#include "launch.hpp"
+#include "tile_io.hpp"
+
+namespace fa {
+
+template <class T, int D, int BN, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(AttnArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int BM = NW * 32;
+  using Tile = TileRegs<D, BN, NT>;
+  constexpr int KP = RowPitch<D>::value;
+  constexpr int VP = ColPitch<BN, Tile::R>::value;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int n_qt = (a.Nq + BM - 1) / BM;
+  const bool heavy_last = (a.causal || a.wr >= 0) && a.wl < 0;
+  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_qt, a.G, heavy_last, a.xcd_remap);
+  const int b = it.unit / a.Hkv, hk = it.unit % a.Hkv;
+  const int hq = hk * a.G + it.sub;
+  const int q0 = it.tile * BM;
+  const int qrow = q0 + wave * 32 + l32;  // the query of this lane's column
+
+  const uint16_t* Qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh;
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + hk * a.v_sh;
+
+  // Q as the B operand of S^T = K Q^T: lane holds d = 16*st + 8*hf + (0..7).
+  u32x4 qf[D / 16];
+  if (qrow < a.Nq) {
+    const uint16_t* qr = Qp + (int64_t)qrow * a.q_sn + 8 * hf;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) qf[st] = *reinterpret_cast<const u32x4*>(qr + 16 * st);
+  } else {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) qf[st] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // Visible keys of this lane's query, and the workgroup's key range.
+  const int lo_i = key_lo(a, qrow), hi_i = key_hi(a, qrow);
+  const int q_last = min(q0 + BM, a.Nq) - 1;
+  const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
+  const int lo_max = key_lo(a, q_last), hi_min = key_hi(a, q0);
+  const int t_lo = kv_lo / BN;
+  const int t_hi = (kv_hi >= kv_lo) ? kv_hi / BN : t_lo - 1;
+
+  const float c = a.scale_log2;
+  float m = -INFINITY, l = 0.f;
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+
+  Tile kt, vt;
+  if (t_lo <= t_hi) {
+    kt.load(Kp, a.k_sn, t_lo * BN, a.Nk, tid);
+    vt.load(Vp, a.v_sn, t_lo * BN, a.Nk, tid);
+  }
+
+  for (int t = t_lo; t <= t_hi; ++t) {
+    const int j0 = t * BN;
+    __syncthreads();  // every wave is done with the previous tile
+    kt.template store_rows<KP>(Ks, tid);
+    vt.template store_cols<VP>(Vt, tid);
+    __syncthreads();
+    if (t < t_hi) {  // next tile's global loads overlap this tile's math
+      kt.load(Kp, a.k_sn, j0 + BN, a.Nk, tid);
+      vt.load(Vp, a.v_sn, j0 + BN, a.Nk, tid);
+    }
+
+    // S^T = K Q^T.  s[kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
+    f32x16 s[BN / 32];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        const u32x4 kf = lds_row8(Ks + (32 * kb + l32) * KP + 16 * st + 8 * hf);
+        s[kb] = T::mfma(kf, qf[st], s[kb]);
+      }
+    }
+
+    // Causal / window / sequence-end masking, only on tiles that need it.
+    const bool full = (j0 >= lo_max) && (j0 + BN - 1 <= hi_min);
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key < lo_i || key > hi_i) s[kb][r] = -INFINITY;
+        }
+      }
+    }
+
+    // Online softmax update.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    }
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2((m - m_use) * c);
+    const float mc = m_use * c;
+
+    u32x4 pf[BN / 16];  // P^T as B operands, one per 16 keys
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(fmaf(s[kb][8 * tt + e], c, -mc));
+          rs += p[e];
+        }
+        pf[2 * kb + tt] = u32x4{T::pack(p[0], p[1]), T::pack(p[2], p[3]), T::pack(p[4], p[5]),
+                                T::pack(p[6], p[7])};
+      }
+    }
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int si = 0; si < BN / 16; ++si) {
+        const u32x4 vf = lds_col8(Vt + (32 * db + l32) * VP + 16 * si + 4 * hf);
+        oacc[db] = T::mfma(vf, pf[si], oacc[db]);
+      }
+    }
+  }
+
+  // Epilogue: O = O / l, LSE = scale*m + ln(l).  Lanes l and l^32 hold
+  // different keys of the same query, so their partial sums are added here.
+  const float lt = l + xor32(l);
+  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+  if (qrow < a.Nq) {
+    uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.o_sb + hq * a.o_sh + (int64_t)qrow * a.o_sn;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * hf;
+        const u32x2 w{T::pack(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv),
+                      T::pack(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + d0) = w;
+      }
+    }
+    if (hf == 0)
+      a.lse[((int64_t)b * a.Hq + hq) * a.Nq + qrow] = (lt > 0.f) ? (m * a.scale + logf(lt)) : -INFINITY;
+  }
+}
+
+template <class T, int D, int BN, int NW>
+static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t stream) {
+  constexpr int BM = NW * 32;
+  const int n_qt = (a.Nq + BM - 1) / BM;
+  const int64_t total = (int64_t)a.B * a.Hkv * n_qt * a.G;
+  if (total == 0) return hipSuccess;
+  AttnArgs args = a;
+  args.xcd_remap = a.xcd_remap && ((a.B * a.Hkv) % 8 == 0);
+  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, NW>), dim3((unsigned)total), dim3(NW * 64), 0,
+                     stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t stream) {
+  if (a.dtype == kBF16) {
+    if (a.D == 128) return launch_fwd_t<BF16, 128, 64, 4>(a, stream);
+    if (a.D == 64) return launch_fwd_t<BF16, 64, 64, 4>(a, stream);
+  } else if (a.dtype == kF16) {
+    if (a.D == 128) return launch_fwd_t<F16, 128, 64, 4>(a, stream);
+    if (a.D == 64) return launch_fwd_t<F16, 64, 64, 4>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

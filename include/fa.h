@@ -1,0 +1,149 @@
+/*
+ * fa.h -- C ABI of the exact tiled attention library for AMD MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention,
+ *
+ *     O = softmax(scale * Q K^T + mask) V,
+ *
+ * one tile of queries against a stream of key/value tiles at a time, with an
+ * online softmax that keeps a running row maximum and row sum, so the
+ * seqlen_q x seqlen_k score matrix never reaches HBM.  The forward pass writes O
+ * and the per-row natural-log log-sum-exp (LSE); the backward pass recomputes
+ * the score tiles from Q, K and the LSE instead of storing probabilities.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P4] "FlashAttention 实战指南:如何把训练内存省 20 倍、速度提 4 倍" (kwkr.cn):
+ *        section "长序列注意力为什么会爆内存" -- the three steps of standard
+ *        attention, tiling into on-chip memory, the online softmax that updates
+ *        the row maximum and sum block by block, and recomputation in the
+ *        backward pass; section "上手 FlashAttention 的三步走" -- tensors are
+ *        (batch, seqlen, nheads, headdim) and causal=True for autoregressive
+ *        use; section "进阶参数如何配置causal、window_size 与 MQA/GQA" --
+ *        window_size (left, right) with -1 meaning unbounded, and K/V head
+ *        counts that divide the Q head count (MQA/GQA).
+ *   [P5] "AI模型推理优化Flash Attention原理" (52runoob.com), section
+ *        "先搞清楚原理" -- scores are scaled by 1/sqrt(headdim) by default.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees, copies or synchronises; kernels are enqueued on
+ *     the caller's HIP stream (hipStream_t passed as void*, NULL = null stream)
+ *     and the call returns before they finish.
+ *   - Layout: q, o, dout, dq are (batch, seqlen_q, nheads_q, headdim); k, v,
+ *     dk, dv are (batch, seqlen_k, nheads_kv, headdim).  Strides are given in
+ *     ELEMENTS for the batch, sequence and head axes; the headdim axis is
+ *     contiguous (stride 1).  lse is a dense float32 array (batch, nheads_q,
+ *     seqlen_q).
+ *   - Masks: query i sees key j iff every active condition holds, with
+ *     i' = i + seqlen_k - seqlen_q (the last query is aligned with the last key):
+ *        causal                ->  j <= i'
+ *        window_left  >= 0     ->  j >= i' - window_left
+ *        window_right >= 0     ->  j <= i' + window_right
+ *     A window bound of -1 is unbounded.  A query that sees no key gets O = 0,
+ *     LSE = -inf and zero gradients.
+ *   - MQA/GQA: query head h reads K/V head h / (nheads_q / nheads_kv).
+ *   - Errors: every argument is validated on the host before any HIP call; a
+ *     non-OK status is returned synchronously and fa_last_error() gives the
+ *     detail (per thread).  No C++ exception crosses this boundary.  Kernel
+ *     faults surface asynchronously on the stream like any HIP work.
+ *   - Thread safety: the library keeps no mutable global state besides a
+ *     per-device capability cache and the per-thread error string.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_VERSION 10000 /* 1.0.0 */
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* malformed input (sizes, null pointers, window < -1, ...) */
+  FA_ERR_UNSUPPORTED = 2, /* valid input this build does not run (headdim, alignment, arch) */
+  FA_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef struct {
+  int64_t batch;
+  int64_t seqlen_q, seqlen_k;
+  int64_t nheads_q, nheads_kv; /* nheads_q must be a multiple of nheads_kv */
+  int64_t headdim;             /* fp16/bf16: 64 or 128; fp32: multiple of 4, 4..128 */
+  /* (batch, seq, head) strides in elements; the headdim axis has stride 1.
+   * In fa_bwd, dout uses o_strides, dq uses q_strides, dk uses k_strides and
+   * dv uses v_strides. */
+  int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3];
+  fa_dtype dtype;       /* element type of q, k, v, o, dout, dq, dk, dv */
+  float scale;          /* > 0 and finite; callers usually pass 1/sqrt(headdim) */
+  int32_t causal;       /* 0 or 1 */
+  int32_t window_left;  /* -1 = unbounded, else >= 0 */
+  int32_t window_right; /* -1 = unbounded, else >= 0 */
+} fa_params;
+
+/*
+ * Forward pass: o = softmax(scale * q k^T + mask) v and lse[b][h][i] =
+ * natural-log log-sum-exp of row i's visible scaled scores ([P4] section
+ * "长序列注意力为什么会爆内存"; the LSE is the final state of the online
+ * softmax's running maximum and sum).
+ *   q [in]  (batch, seqlen_q, nheads_q, headdim), dtype
+ *   k [in]  (batch, seqlen_k, nheads_kv, headdim), dtype
+ *   v [in]  same shape as k
+ *   o [out] same shape as q (o_strides), dtype; must not alias q, k or v
+ *   lse [out] float32 (batch, nheads_q, seqlen_q), dense
+ *   stream  hipStream_t or NULL
+ * Requirements: all pointers 16-byte aligned and every stride a multiple of
+ * 16 bytes (else FA_ERR_UNSUPPORTED).  Results are bitwise repeatable for
+ * identical inputs and launch configuration.
+ */
+fa_status fa_fwd(const fa_params* params, const void* q, const void* k, const void* v,
+                 void* o, float* lse, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these parameters (a float32
+ * per-row array D_i = sum_c dout[i,c] * o[i,c], batch * nheads_q * seqlen_q
+ * entries, rounded up to 256 bytes).  Writes the size to *bytes.
+ */
+fa_status fa_bwd_workspace_size(const fa_params* params, size_t* bytes);
+
+/*
+ * Backward pass: gradients of L = sum(o * dout) with respect to q, k and v,
+ * recomputing the probability tiles from q, k and lse ([P4] section
+ * "长序列注意力为什么会爆内存": the backward pass does not keep the attention
+ * matrix and recomputes it when needed):
+ *     dP = dout v^T,  D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
+ *     dq = scale dS k,  dk = scale dS^T q,  dv = P^T dout,
+ * with dk and dv summed over the query heads of a K/V head group.
+ *   dout [in] same shape/layout as o (o_strides), dtype
+ *   q, k, v [in] as in fa_fwd
+ *   o [in]  the forward output (o_strides), dtype
+ *   lse [in] the forward LSE, float32 (batch, nheads_q, seqlen_q)
+ *   dq [out] shape of q (q_strides); dk, dv [out] shape of k (k_strides,
+ *            v_strides).  Outputs are fully overwritten (no accumulation).
+ *   workspace [scratch] device memory of at least fa_bwd_workspace_size bytes,
+ *            256-byte aligned, owned by the caller; contents are clobbered.
+ * The gradients are computed without atomics, so they are bitwise repeatable.
+ */
+fa_status fa_bwd(const fa_params* params, const void* dout, const void* q, const void* k,
+                 const void* v, const void* o, const float* lse, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static string naming a status code. */
+const char* fa_status_string(fa_status status);
+
+/* Detail message of the last non-OK status returned on this thread ("" if none). */
+const char* fa_last_error(void);
+
+/* FA_VERSION of the built library. */
+int fa_version(void);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* FA_H_ */
