@@ -24,6 +24,8 @@
 //                 S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T
 // The dQ kernel recomputes S and dP (7 tile products per score pair instead of
 // 5) in exchange for no atomic accumulation and no dQ workspace.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile_io.hpp"
@@ -39,7 +41,9 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a) {
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   const int64_t rows = (int64_t)a.B * a.Nq * a.Hq;
-  float acc = 0.f;
+  // fp32 inputs accumulate in float64 (exact products); 16-bit inputs in fp32.
+  using Acc = typename std::conditional<ELT == 4, double, float>::type;
+  Acc acc = 0;
   int h = 0, i = 0, b = 0;
   if (row < rows) {
     h = (int)(row % a.Hq);
@@ -55,7 +59,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         if constexpr (ELT == 4) {
-          acc = fmaf(__uint_as_float(x[w]), __uint_as_float(y[w]), acc);
+          acc = fma((double)__uint_as_float(x[w]), (double)__uint_as_float(y[w]), acc);
         } else if (a.dtype == kBF16) {
           acc = fmaf(BF16::to_f32(x[w] & 0xffffu), BF16::to_f32(y[w] & 0xffffu), acc);
           acc = fmaf(BF16::to_f32(x[w] >> 16), BF16::to_f32(y[w] >> 16), acc);
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-  if (row < rows && sub == 0) a.dsum[((int64_t)b * a.Hq + h) * a.Nq + i] = acc;
+  if (row < rows && sub == 0) a.dsum[((int64_t)b * a.Hq + h) * a.Nq + i] = (float)acc;
 }
 
 hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {

@@ -8,6 +8,11 @@
 // in 16 consecutive lanes and are reduced with 4 lane exchanges.
 // D is a runtime value (multiple of 4, at most DP); LDS rows are padded to an
 // odd pitch so that 16 lanes reading 16 different rows hit 16 different banks.
+// Every dot product and long accumulation (scores, dP, O, the row sums, dQ, dK,
+// dV) is carried in float64: a product of two fp32 values is exact in fp64,
+// and on gfx950 a float64 FMA issues at the same rate as an unpacked fp32 one.
+// Sums over thousands of keys or queries therefore round only once, and the
+// exponent argument (s - m)*scale*log2(e) is formed before rounding to fp32.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -35,16 +40,16 @@ __device__ __forceinline__ void load_rows_f32(float* dst, const float* base, int
   }
 }
 
-// acc[ii][jj] = sum_c A[tr+16ii][c] * B[tc+16jj][c]   (A, B row-major in LDS)
+// acc[ii][jj] = sum_c A[tr+16ii][c] * B[tc+16jj][c]   (A, B row-major in LDS), in float64
 template <int P>
-__device__ __forceinline__ void tile_abt(float (&acc)[4][4], const float* A, const float* B, int D, int tr,
+__device__ __forceinline__ void tile_abt(double (&acc)[4][4], const float* A, const float* B, int D, int tr,
                                          int tc) {
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) acc[ii][jj] = 0.f;
+    for (int jj = 0; jj < 4; ++jj) acc[ii][jj] = 0.0;
   for (int c = 0; c < D; ++c) {
-    float x[4], y[4];
+    double x[4], y[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) x[ii] = A[(tr + 16 * ii) * P + c];
 #pragma unroll
@@ -52,16 +57,17 @@ __device__ __forceinline__ void tile_abt(float (&acc)[4][4], const float* A, con
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) acc[ii][jj] = fmaf(x[ii], y[jj], acc[ii][jj]);
+      for (int jj = 0; jj < 4; ++jj) acc[ii][jj] = fma(x[ii], y[jj], acc[ii][jj]);
   }
 }
 
-// out[ii][jj] += sum_k W[tr+16ii][k] * X[k][tc+16jj]  (W: kT x kT, pitch kT+1; X pitch P)
+// out[ii][jj] += sum_k W[tr+16ii][k] * X[k][tc+16jj]  (W: kT x kT, pitch kT+1; X pitch P),
+// accumulated in float64.
 template <int DP, int P>
-__device__ __forceinline__ void tile_wx(float (&out)[4][DP / 16], const float* W, const float* X, int tr,
+__device__ __forceinline__ void tile_wx(double (&out)[4][DP / 16], const float* W, const float* X, int tr,
                                         int tc) {
   for (int k = 0; k < kT; ++k) {
-    float w[4], x[DP / 16];
+    double w[4], x[DP / 16];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) w[ii] = W[(tr + 16 * ii) * (kT + 1) + k];
 #pragma unroll
@@ -69,13 +75,13 @@ __device__ __forceinline__ void tile_wx(float (&out)[4][DP / 16], const float* W
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-      for (int jj = 0; jj < DP / 16; ++jj) out[ii][jj] = fmaf(w[ii], x[jj], out[ii][jj]);
+      for (int jj = 0; jj < DP / 16; ++jj) out[ii][jj] = fma(w[ii], x[jj], out[ii][jj]);
   }
 }
 
-__device__ __forceinline__ float row16_max(float x) {
+__device__ __forceinline__ double row16_max(double x) {
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 16));
+  for (int off = 8; off >= 1; off >>= 1) x = fmax(x, __shfl_xor(x, off, 16));
   return x;
 }
 __device__ __forceinline__ float row16_sum(float x) {
@@ -86,7 +92,7 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 template <int DP>
 __device__ __forceinline__ void store_rows_f32(float* base, int64_t stride, int row0, int nrows, int D,
-                                               const float (&v)[4][DP / 16], float mul, int tr, int tc) {
+                                               const double (&v)[4][DP / 16], double mul, int tr, int tc) {
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int r = row0 + tr + 16 * ii;
@@ -94,7 +100,7 @@ __device__ __forceinline__ void store_rows_f32(float* base, int64_t stride, int 
 #pragma unroll
     for (int jj = 0; jj < DP / 16; ++jj) {
       const int cidx = tc + 16 * jj;
-      if (cidx < D) base[(int64_t)r * stride + cidx] = v[ii][jj] * mul;
+      if (cidx < D) base[(int64_t)r * stride + cidx] = (float)(v[ii][jj] * mul);
     }
   }
 }
@@ -121,21 +127,22 @@ __global__ __launch_bounds__(256) void f32_fwd_kernel(AttnArgs a) {
 
   load_rows_f32<DP, P>(Qs, Qp, a.q_sn, q0, a.Nq, a.D, tid);
   int lo[4], hi[4];
-  float m[4], l[4];
-  float o[4][DP / 16];
+  double m[4];
+  double l[4];
+  double o[4][DP / 16];
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     lo[ii] = key_lo(a, q0 + tr + 16 * ii);
     hi[ii] = key_hi(a, q0 + tr + 16 * ii);
     m[ii] = -INFINITY;
-    l[ii] = 0.f;
+    l[ii] = 0.0;
 #pragma unroll
-    for (int jj = 0; jj < DP / 16; ++jj) o[ii][jj] = 0.f;
+    for (int jj = 0; jj < DP / 16; ++jj) o[ii][jj] = 0.0;
   }
   const int q_last = min(q0 + kT, a.Nq) - 1;
   const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
   const int t_lo = kv_lo / kT, t_hi = (kv_hi >= kv_lo) ? kv_hi / kT : t_lo - 1;
-  const float c = a.scale_log2;
+  const double c = (double)a.scale * 1.4426950408889634;
 
   for (int t = t_lo; t <= t_hi; ++t) {
     const int j0 = t * kT;
@@ -143,32 +150,32 @@ __global__ __launch_bounds__(256) void f32_fwd_kernel(AttnArgs a) {
     load_rows_f32<DP, P>(Ks, Kp, a.k_sn, j0, a.Nk, a.D, tid);
     load_rows_f32<DP, P>(Vs, Vp, a.v_sn, j0, a.Nk, a.D, tid);
     __syncthreads();
-    float s[4][4];
+    double s[4][4];
     tile_abt<P>(s, Qs, Ks, a.D, tr, tc);
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      float mx = -INFINITY;
+      double mx = -INFINITY;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int key = j0 + tc + 16 * jj;
         if (key < lo[ii] || key > hi[ii]) s[ii][jj] = -INFINITY;
-        mx = fmaxf(mx, s[ii][jj]);
+        mx = fmax(mx, s[ii][jj]);
       }
       mx = row16_max(mx);
-      const float m_new = fmaxf(m[ii], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2((m[ii] - m_use) * c);
+      const double m_new = fmax(m[ii], mx);
+      const double m_use = (m_new == -INFINITY) ? 0.0 : m_new;
+      const float alpha = fast_exp2((float)((m[ii] - m_use) * c));
       float rs = 0.f;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const float p = fast_exp2(fmaf(s[ii][jj], c, -m_use * c));
+        const float p = fast_exp2((float)((s[ii][jj] - m_use) * c));
         rs += p;
         Ps[(tr + 16 * ii) * (kT + 1) + tc + 16 * jj] = p;
       }
-      l[ii] = l[ii] * alpha + row16_sum(rs);
+      l[ii] = l[ii] * (double)alpha + (double)row16_sum(rs);
       m[ii] = m_new;
 #pragma unroll
-      for (int jj = 0; jj < DP / 16; ++jj) o[ii][jj] *= alpha;
+      for (int jj = 0; jj < DP / 16; ++jj) o[ii][jj] *= (double)alpha;
     }
     __syncthreads();
     tile_wx<DP, P>(o, Ps, Vs, tr, tc);
@@ -178,15 +185,15 @@ __global__ __launch_bounds__(256) void f32_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int r = q0 + tr + 16 * ii;
-    const float inv = (l[ii] > 0.f) ? 1.f / l[ii] : 0.f;
     if (r < a.Nq) {
 #pragma unroll
       for (int jj = 0; jj < DP / 16; ++jj) {
         const int cidx = tc + 16 * jj;
-        if (cidx < a.D) Op[(int64_t)r * a.o_sn + cidx] = o[ii][jj] * inv;
+        if (cidx < a.D) Op[(int64_t)r * a.o_sn + cidx] = (l[ii] > 0.0) ? (float)(o[ii][jj] / l[ii]) : 0.f;
       }
       if (tc == 0)
-        a.lse[((int64_t)b * a.Hq + hq) * a.Nq + r] = (l[ii] > 0.f) ? (m[ii] * a.scale + logf(l[ii])) : -INFINITY;
+        a.lse[((int64_t)b * a.Hq + hq) * a.Nq + r] =
+            (l[ii] > 0.0) ? (float)(m[ii] * a.scale + log(l[ii])) : -INFINITY;
     }
   }
 }
@@ -213,8 +220,8 @@ __global__ __launch_bounds__(256) void f32_bwd_dq_kernel(AttnArgs a) {
   load_rows_f32<DP, P>(dOs, dOp, a.o_sn, q0, a.Nq, a.D, tid);
 
   int lo[4], hi[4];
-  float lse2[4], dsum[4];
-  float dq[4][DP / 16];
+  double lse2[4], dsum[4];
+  double dq[4][DP / 16];
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const int r = q0 + tr + 16 * ii;
@@ -222,15 +229,15 @@ __global__ __launch_bounds__(256) void f32_bwd_dq_kernel(AttnArgs a) {
     hi[ii] = key_hi(a, r);
     const int64_t ri = ((int64_t)b * a.Hq + hq) * a.Nq + r;
     const float L = (r < a.Nq) ? a.lse[ri] : -INFINITY;
-    lse2[ii] = (L == -INFINITY) ? INFINITY : L * kLog2e;
-    dsum[ii] = (r < a.Nq) ? a.dsum[ri] : 0.f;
+    lse2[ii] = (L == -INFINITY) ? INFINITY : (double)L * 1.4426950408889634;
+    dsum[ii] = (r < a.Nq) ? (double)a.dsum[ri] : 0.0;
 #pragma unroll
-    for (int jj = 0; jj < DP / 16; ++jj) dq[ii][jj] = 0.f;
+    for (int jj = 0; jj < DP / 16; ++jj) dq[ii][jj] = 0.0;
   }
   const int q_last = min(q0 + kT, a.Nq) - 1;
   const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
   const int t_lo = kv_lo / kT, t_hi = (kv_hi >= kv_lo) ? kv_hi / kT : t_lo - 1;
-  const float c = a.scale_log2;
+  const double c = (double)a.scale * 1.4426950408889634;
 
   for (int t = t_lo; t <= t_hi; ++t) {
     const int j0 = t * kT;
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(256) void f32_bwd_dq_kernel(AttnArgs a) {
     load_rows_f32<DP, P>(Ks, Kp, a.k_sn, j0, a.Nk, a.D, tid);
     load_rows_f32<DP, P>(Vs, Vp, a.v_sn, j0, a.Nk, a.D, tid);
     __syncthreads();
-    float s[4][4], dp[4][4];
+    double s[4][4], dp[4][4];
     tile_abt<P>(s, Qs, Ks, a.D, tr, tc);
     tile_abt<P>(dp, dOs, Vs, a.D, tr, tc);
 #pragma unroll
@@ -247,15 +254,15 @@ __global__ __launch_bounds__(256) void f32_bwd_dq_kernel(AttnArgs a) {
       for (int jj = 0; jj < 4; ++jj) {
         const int key = j0 + tc + 16 * jj;
         const bool vis = key >= lo[ii] && key <= hi[ii];
-        const float p = vis ? fast_exp2(fmaf(s[ii][jj], c, -lse2[ii])) : 0.f;
-        Ps[(tr + 16 * ii) * (kT + 1) + tc + 16 * jj] = p * (dp[ii][jj] - dsum[ii]);
+        const double p = vis ? (double)fast_exp2((float)(s[ii][jj] * c - lse2[ii])) : 0.0;
+        Ps[(tr + 16 * ii) * (kT + 1) + tc + 16 * jj] = (float)(p * (dp[ii][jj] - dsum[ii]));
       }
     }
     __syncthreads();
     tile_wx<DP, P>(dq, Ps, Ks, tr, tc);
   }
   float* dQp = static_cast<float*>(a.dq) + b * a.q_sb + hq * a.q_sh;
-  store_rows_f32<DP>(dQp, a.q_sn, q0, a.Nq, a.D, dq, a.scale, tr, tc);
+  store_rows_f32<DP>(dQp, a.q_sn, q0, a.Nq, a.D, dq, (double)a.scale, tr, tc);
 }
 
 // ---------------------------------------------------------------------------
@@ -265,7 +272,7 @@ template <int DP>
 __global__ __launch_bounds__(256) void f32_bwd_dkdv_kernel(AttnArgs a) {
   constexpr int P = DP + 1;
   __shared__ float Ks[kT * P], Vs[kT * P], Qs[kT * P], dOs[kT * P], Ps[kT * (kT + 1)];
-  __shared__ float lse2s[kT], dsums[kT];
+  __shared__ double lse2s[kT], dsums[kT];
   const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
   const int n_kt = (a.Nk + kT - 1) / kT;
   const int kt = blockIdx.x % n_kt;
@@ -277,16 +284,16 @@ __global__ __launch_bounds__(256) void f32_bwd_dkdv_kernel(AttnArgs a) {
   load_rows_f32<DP, P>(Ks, Kp, a.k_sn, k0, a.Nk, a.D, tid);
   load_rows_f32<DP, P>(Vs, Vp, a.v_sn, k0, a.Nk, a.D, tid);
 
-  float dk[4][DP / 16], dv[4][DP / 16];
+  double dk[4][DP / 16], dv[4][DP / 16];
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-    for (int jj = 0; jj < DP / 16; ++jj) dk[ii][jj] = dv[ii][jj] = 0.f;
+    for (int jj = 0; jj < DP / 16; ++jj) dk[ii][jj] = dv[ii][jj] = 0.0;
 
   const int k_last = min(k0 + kT, a.Nk) - 1;
   const int i_lo = query_lo(a, k0), i_hi = query_hi(a, k_last);
   const int t_lo = i_lo / kT, t_hi = (i_hi >= i_lo) ? i_hi / kT : t_lo - 1;
-  const float c = a.scale_log2;
+  const double c = (double)a.scale * 1.4426950408889634;
 
   for (int g = 0; g < a.G; ++g) {
     const int hq = hk * a.G + g;
@@ -301,26 +308,27 @@ __global__ __launch_bounds__(256) void f32_bwd_dkdv_kernel(AttnArgs a) {
       if (tid < kT) {
         const int i = i0 + tid;
         const float L = (i < a.Nq) ? a.lse[rbase + i] : -INFINITY;
-        lse2s[tid] = (L == -INFINITY) ? INFINITY : L * kLog2e;
-        dsums[tid] = (i < a.Nq) ? a.dsum[rbase + i] : 0.f;
+        lse2s[tid] = (L == -INFINITY) ? INFINITY : (double)L * 1.4426950408889634;
+        dsums[tid] = (i < a.Nq) ? (double)a.dsum[rbase + i] : 0.0;
       }
       __syncthreads();
       // S^T[key][query] and dP^T[key][query].
-      float s[4][4], dp[4][4], ds[4][4];
+      double s[4][4], dp[4][4];
+      float ds[4][4];
       tile_abt<P>(s, Ks, Qs, a.D, tr, tc);
       tile_abt<P>(dp, Vs, dOs, a.D, tr, tc);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int i = i0 + tc + 16 * jj;
         const int lo = key_lo(a, i), hi = key_hi(a, i);
-        const float l2 = lse2s[tc + 16 * jj], dd = dsums[tc + 16 * jj];
+        const double l2 = lse2s[tc + 16 * jj], dd = dsums[tc + 16 * jj];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int key = k0 + tr + 16 * ii;
           const bool vis = key >= lo && key <= hi;
-          const float p = vis ? fast_exp2(fmaf(s[ii][jj], c, -l2)) : 0.f;
+          const float p = vis ? fast_exp2((float)(s[ii][jj] * c - l2)) : 0.f;
           Ps[(tr + 16 * ii) * (kT + 1) + tc + 16 * jj] = p;
-          ds[ii][jj] = p * (dp[ii][jj] - dd);
+          ds[ii][jj] = (float)((double)p * (dp[ii][jj] - dd));
         }
       }
       __syncthreads();
@@ -336,8 +344,8 @@ __global__ __launch_bounds__(256) void f32_bwd_dkdv_kernel(AttnArgs a) {
   }
   float* dKp = static_cast<float*>(a.dk) + b * a.k_sb + hk * a.k_sh;
   float* dVp = static_cast<float*>(a.dv) + b * a.v_sb + hk * a.v_sh;
-  store_rows_f32<DP>(dKp, a.k_sn, k0, a.Nk, a.D, dk, a.scale, tr, tc);
-  store_rows_f32<DP>(dVp, a.v_sn, k0, a.Nk, a.D, dv, 1.f, tr, tc);
+  store_rows_f32<DP>(dKp, a.k_sn, k0, a.Nk, a.D, dk, (double)a.scale, tr, tc);
+  store_rows_f32<DP>(dVp, a.v_sn, k0, a.Nk, a.D, dv, 1.0, tr, tc);
 }
 
 // ---------------------------------------------------------------------------

@@ -6,6 +6,7 @@ import torch
 
 import exact_tiled_attention_07_amd as fa
 import oracle
+from compare import within
 
 # Max-abs tolerances of the HIP path against the float64 oracle: O and LSE
 # use the first, dQ/dK/dV twice it.
@@ -26,6 +27,17 @@ def max_err(got, ref):
     fin = ~inf_ref
     assert np.all(np.isfinite(got[fin])), "non-finite values in the GPU result"
     return float(np.max(np.abs(got[fin] - ref[fin]))) if fin.any() else 0.0
+
+
+DTYPE_NAME = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}
+
+
+def assert_close(got, ref, tol, what):
+    """Oracle comparison rule of compare.py for a GPU tensor against a float64 array."""
+    ok, info = within(f64(got), ref, DTYPE_NAME[got.dtype], tol)
+    assert ok, f"{what}: raw {info['raw']:.3e}, excess over output rounding {info['excess']:.3e}, " \
+               f"raw where |ref|<4 {info['raw_small']:.3e}; tolerance {tol:.1e}"
+    return info
 
 
 def gpu_fwd(q, k, v, **kw):
@@ -49,9 +61,8 @@ def check_fwd(q, k, v, tol_mult=1.0, **kw):
     o, lse = gpu_fwd(q, k, v, **kw)
     o_ref, lse_ref = oracle.attention_fwd(f64(q), f64(k), f64(v), **oracle_kw(kw))
     tol = TOL[q.dtype] * tol_mult
-    eo, el = max_err(f64(o), o_ref), max_err(f64(lse), lse_ref)
-    assert eo <= tol, f"O max-abs error {eo:.3e} > {tol:.1e}"
-    assert el <= tol, f"LSE max-abs error {el:.3e} > {tol:.1e}"
+    eo = assert_close(o, o_ref, tol, "O")
+    el = assert_close(lse, lse_ref, tol, "LSE")
     return o, lse, eo, el
 
 
@@ -62,6 +73,5 @@ def check_bwd(q, k, v, do, **kw):
     tol = 2 * TOL[q.dtype]
     errs = {}
     for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
-        errs[name] = max_err(f64(got), r)
-        assert errs[name] <= tol, f"{name} max-abs error {errs[name]:.3e} > {tol:.1e}"
+        errs[name] = assert_close(got, r, tol, name)
     return errs
