@@ -33,7 +33,25 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (whole heads are added until it is reached)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="instead of the benchmark, run a plain device copy of 512 MiB (read 512 MiB, "
+                         "write 512 MiB) 5 times: the known-size reference for HBM byte counters")
     return ap.parse_args()
+
+
+def copy_probe():
+    import torch
+    n = 512 << 20
+    x = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                      "copy_GBps": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
 def visible_pairs(n, causal, window):
@@ -69,17 +87,21 @@ def cpu_baseline(w, q, k, v, do, budget_s):
     except Exception:  # pragma: no cover
         blas_threads = None
     G = w.nheads_q // w.nheads_kv
-    kf = k[0:1, :, 0:1].double().numpy()
-    vf = v[0:1, :, 0:1].double().numpy()
     done, t_total = 0, 0.0
-    for h in range(G):
-        qf = q[0:1, :, h:h + 1].double().numpy()
-        dof = do[0:1, :, h:h + 1].double().numpy()
-        t0 = time.perf_counter()
-        oracle.attention_fwd(qf, kf, vf, causal=w.causal, window=w.window)
-        oracle.attention_bwd(dof, qf, kf, vf, causal=w.causal, window=w.window)
-        t_total += time.perf_counter() - t0
-        done += 1
+    for b in range(w.batch):
+        for h in range(w.nheads_q):
+            g = h // G
+            kf = k[b:b + 1, :, g:g + 1].double().numpy()
+            vf = v[b:b + 1, :, g:g + 1].double().numpy()
+            qf = q[b:b + 1, :, h:h + 1].double().numpy()
+            dof = do[b:b + 1, :, h:h + 1].double().numpy()
+            t0 = time.perf_counter()
+            oracle.attention_fwd(qf, kf, vf, causal=w.causal, window=w.window)
+            oracle.attention_bwd(dof, qf, kf, vf, causal=w.causal, window=w.window)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total >= budget_s:
+                break
         if t_total >= budget_s:
             break
     f_head = sum(flops(w)) / (w.batch * w.nheads_q)
@@ -96,7 +118,7 @@ def cpu_baseline(w, q, k, v, do, budget_s):
         "unit": "TFLOP/s",
         "cores": blas_threads or len(os.sched_getaffinity(0)),
         "kind": "oracle",
-        "sample": f"{done} query head(s) x {w.seqlen} rows of batch 0 / kv head 0, fwd+bwd, float64 "
+        "sample": f"{done} of {w.batch * w.nheads_q} (batch, query head) pairs x {w.seqlen} rows, fwd+bwd, float64 "
                   f"NumPy oracle ({t_total:.1f} s; {len(os.sched_getaffinity(0))} cores in affinity mask, "
                   f"CPU: {cpu_model})",
     }
@@ -104,6 +126,9 @@ def cpu_baseline(w, q, k, v, do, budget_s):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

@@ -19,21 +19,29 @@
 // The O rescale by exp(m_old - m_new) is a per-lane scalar (one query per lane).
 // Scores are kept in raw units; exp(scale*(s - m)) is evaluated as
 // exp2(s*c - m*c) with c = scale*log2(e), one FMA and one v_exp_f32.
+// K and V tiles sit in LDS row-major with a chunk swizzle (tile_io.hpp), double
+// buffered so that one barrier per tile suffices; V^T operands come straight
+// from the row-major tile through the transposing LDS read.
 #include "common.hpp"
 #include "launch.hpp"
 #include "tile_io.hpp"
 
 namespace fa {
 
+// Largest growth of the row maximum (in log2 units) absorbed without
+// rescaling O and l: until the maximum has grown by more than this, the stale
+// maximum keeps being the reference, so probabilities stay below 2^kLazyRescale.
+// O and l always share the same reference, so the result is unchanged.
+static constexpr float kLazyRescale = 8.0f;
+
 template <class T, int D, int BN, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_mfma_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
-  using Tile = TileRegs<D, BN, NT>;
-  constexpr int KP = RowPitch<D>::value;
-  constexpr int VP = ColPitch<BN, Tile::R>::value;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  constexpr int TILE = BN * D;  // elements of one K or V tile
+  using Tile = SwzTile<D, BN, NT>;
+  // Two buffers, each holding one K tile and one V tile (swizzled row-major).
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -71,27 +79,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int t_hi = (kv_hi >= kv_lo) ? kv_hi / BN : t_lo - 1;
 
   const float c = a.scale_log2;
-  float m = -INFINITY, l = 0.f;
+  float mref = -INFINITY;  // reference maximum of the exponentials (raw score units)
+  float l = 0.f;           // this lane's partial row sum (its 16 keys of every 32)
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
 
   Tile kt, vt;
+  kt.init(tid);
+  vt.init(tid);
   if (t_lo <= t_hi) {
-    kt.load(Kp, a.k_sn, t_lo * BN, a.Nk, tid);
-    vt.load(Vp, a.v_sn, t_lo * BN, a.Nk, tid);
+    kt.load(Kp, a.k_sn, t_lo * BN, a.Nk);
+    vt.load(Vp, a.v_sn, t_lo * BN, a.Nk);
+    kt.store(smem);
+    vt.store(smem + TILE);
+  }
+  __syncthreads();
+  if (t_lo + 1 <= t_hi) {
+    kt.load(Kp, a.k_sn, (t_lo + 1) * BN, a.Nk);
+    vt.load(Vp, a.v_sn, (t_lo + 1) * BN, a.Nk);
   }
 
   for (int t = t_lo; t <= t_hi; ++t) {
     const int j0 = t * BN;
-    __syncthreads();  // every wave is done with the previous tile
-    kt.template store_rows<KP>(Ks, tid);
-    vt.template store_cols<VP>(Vt, tid);
-    __syncthreads();
-    if (t < t_hi) {  // next tile's global loads overlap this tile's math
-      kt.load(Kp, a.k_sn, j0 + BN, a.Nk, tid);
-      vt.load(Vp, a.v_sn, j0 + BN, a.Nk, tid);
-    }
+    const int buf = (t - t_lo) & 1;
+    const uint16_t* Ks = smem + buf * 2 * TILE;
+    const uint16_t* Vs = Ks + TILE;
 
     // S^T = K Q^T.  s[kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
     f32x16 s[BN / 32];
@@ -100,10 +113,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-        const u32x4 kf = lds_row8(Ks + (32 * kb + l32) * KP + 16 * st + 8 * hf);
-        s[kb] = T::mfma(kf, qf[st], s[kb]);
-      }
+      for (int kb = 0; kb < BN / 32; ++kb)
+        s[kb] = T::mfma(swz_chunk<D>(Ks, 32 * kb + l32, 2 * st + hf), qf[st], s[kb]);
     }
 
     // Causal / window / sequence-end masking, only on tiles that need it.
@@ -119,7 +130,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
     }
 
-    // Online softmax update.
+    // Online softmax.  The reference maximum moves only when some row of the
+    // wave grew by more than 2^kLazyRescale; then O and l are rescaled.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
@@ -127,13 +139,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     }
     mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2((m - m_use) * c);
-    const float mc = m_use * c;
+    const bool grow = (mx - mref) * c > kLazyRescale;  // false for NaN (both -inf)
+    if (__any(grow)) {
+      const float m_new = fmaxf(mref, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((mref - m_new) * c);
+      mref = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    }
+    const float mc = (mref == -INFINITY) ? 0.f : mref * c;
 
     u32x4 pf[BN / 16];  // P^T as B operands, one per 16 keys
-    float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
@@ -142,29 +159,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           p[e] = fast_exp2(fmaf(s[kb][8 * tt + e], c, -mc));
-          rs += p[e];
+          l += p[e];
         }
         pf[2 * kb + tt] = u32x4{T::pack(p[0], p[1]), T::pack(p[2], p[3]), T::pack(p[4], p[5]),
                                 T::pack(p[6], p[7])};
       }
     }
-    l = l * alpha + rs;
-    m = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
 
-    // O^T += V^T P^T.
+    // O^T += V^T P^T, V^T read transposed from the row-major tile.
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int si = 0; si < BN / 16; ++si) {
 #pragma unroll
-      for (int si = 0; si < BN / 16; ++si) {
-        const u32x4 vf = lds_col8(Vt + (32 * db + l32) * VP + 16 * si + 4 * hf);
-        oacc[db] = T::mfma(vf, pf[si], oacc[db]);
-      }
+      for (int db = 0; db < D / 32; ++db)
+        oacc[db] = T::mfma(swz_tr_operand<D>(Vs, si, db, lane), pf[si], oacc[db]);
+    }
+
+    // Stage the next tile into the other buffer (last read one iteration ago).
+    if (t < t_hi) {
+      kt.store(smem + (buf ^ 1) * 2 * TILE);
+      vt.store(smem + (buf ^ 1) * 2 * TILE + TILE);
+    }
+    __syncthreads();
+    if (t + 2 <= t_hi) {
+      kt.load(Kp, a.k_sn, j0 + 2 * BN, a.Nk);
+      vt.load(Vp, a.v_sn, j0 + 2 * BN, a.Nk);
     }
   }
 
-  // Epilogue: O = O / l, LSE = scale*m + ln(l).  Lanes l and l^32 hold
+  // Epilogue: O = O / l, LSE = scale*mref + ln(l).  Lanes l and l^32 hold
   // different keys of the same query, so their partial sums are added here.
   const float lt = l + xor32(l);
   const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
@@ -181,7 +203,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
     }
     if (hf == 0)
-      a.lse[((int64_t)b * a.Hq + hq) * a.Nq + qrow] = (lt > 0.f) ? (m * a.scale + logf(lt)) : -INFINITY;
+      a.lse[((int64_t)b * a.Hq + hq) * a.Nq + qrow] = (lt > 0.f) ? (mref * a.scale + logf(lt)) : -INFINITY;
   }
 }
 

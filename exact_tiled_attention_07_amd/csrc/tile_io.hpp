@@ -96,4 +96,104 @@ __device__ __forceinline__ u32x4 lds_col8(const uint16_t* p) {
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// ===========================================================================
+// Swizzled row-major tiles (no padding, no transposed copy).
+//
+// A tile of ROWS x D 16-bit elements is stored row-major with its 16-byte
+// chunks permuted inside each row: chunk c of row r sits at chunk position
+// c ^ sw(r).  The permutation makes three access patterns free of LDS bank
+// conflicts (64 banks x 4 bytes):
+//   * 16-byte row-chunk reads by 16 lanes on 16 consecutive rows (the MFMA
+//     operand whose lanes run along the rows),
+//   * transposing 8-byte reads (ds_read_b64_tr_b16) of 4 consecutive rows x
+//     4 consecutive chunks per 32 lanes (the MFMA operand whose reduction axis
+//     runs along the rows),
+//   * the 16-byte chunk writes of the loader.
+// ===========================================================================
+template <int D>
+struct Swz {
+  static_assert(D == 64 || D == 128, "swizzle defined for D = 64, 128");
+  __device__ __forceinline__ static int sw(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+  // Byte offset of logical chunk c (8 elements) of row r.
+  __device__ __forceinline__ static int off(int r, int c) { return r * (2 * D) + 16 * (c ^ sw(r)); }
+};
+
+// Global -> registers -> swizzled LDS.  Thread t holds chunk cc = t % CPR of
+// rows a + i * (NT / CPR), a = t / CPR, i < R; for a fixed i consecutive
+// threads read consecutive 16-byte chunks of consecutive rows.
+template <int D, int ROWS, int NT>
+struct SwzTile {
+  static constexpr int CPR = D / 8;
+  static constexpr int RSTRIDE = NT / CPR;
+  static constexpr int R = ROWS / RSTRIDE;
+  static_assert(ROWS % RSTRIDE == 0 && R >= 1, "tile does not divide over the threads");
+  u32x4 r[R];
+  int a, cc;
+
+  __device__ __forceinline__ void init(int tid) {
+    a = tid / CPR;
+    cc = tid % CPR;
+  }
+  // Rows row0 .. row0+ROWS-1 of a tensor whose row i starts at base + i*stride.
+  // Rows at or beyond nrows (>= 1) re-read row nrows-1: such keys are always
+  // masked (or are queries whose results are discarded), and a finite copy
+  // keeps 0 * value finite.
+  __device__ __forceinline__ void load(const uint16_t* base, int64_t stride, int row0, int nrows) {
+    const uint16_t* p = base + (int64_t)row0 * stride + (int64_t)a * stride + cc * 8;
+    if (row0 + ROWS <= nrows) {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        r[i] = *reinterpret_cast<const u32x4*>(p + (int64_t)(i * RSTRIDE) * stride);
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int row = min(row0 + a + i * RSTRIDE, nrows - 1);
+        r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)row * stride + cc * 8);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* tile) const {
+    char* t = reinterpret_cast<char*>(tile);
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      *reinterpret_cast<u32x4*>(t + Swz<D>::off(a + i * RSTRIDE, cc)) = r[i];
+  }
+};
+
+// 8 consecutive elements (logical chunk c) of row r: an MFMA operand whose
+// lanes run along the rows.
+template <int D>
+__device__ __forceinline__ u32x4 swz_chunk(const uint16_t* tile, int r, int c) {
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(tile) + Swz<D>::off(r, c));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// MFMA operand whose reduction axis runs along the rows, for rows 16*s .. 16*s+15
+// and columns 32*db .. 32*db+31 of a swizzled tile: lane (l32, hf) receives
+// columns 32*db + l32 of rows 16*s + {4hf..4hf+3, 8+4hf..8+4hf+3} -- the key
+// order of a 32x32 accumulator's registers 0..7 (or 8..15) in that lane.
+// ds_read_b64_tr_b16 hands lane i of each 16-lane group element i%4 of the
+// 4-element chunks that lanes {i/4, 4+i/4, 8+i/4, 12+i/4} point to; so lane j
+// of a group points at row (j/4) of its 4-row block, columns 4*(j%4)..+3 of
+// its 16-column half.
+template <int D>
+__device__ __forceinline__ u32x4 swz_tr_operand(const uint16_t* tile, int s, int db, int lane) {
+  const int G = lane >> 4, j = lane & 15;
+  const int hf = G >> 1, gsub = G & 1, ep = j >> 2, q = j & 3;
+  const int r0 = 16 * s + 4 * hf + ep;
+  const int c = 4 * db + 2 * gsub + (q >> 1);
+  const char* t = reinterpret_cast<const char*>(tile);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(t + Swz<D>::off(r0, c) + 8 * (q & 1)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(t + Swz<D>::off(r0 + 8, c) + 8 * (q & 1)));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
 }  // namespace fa
