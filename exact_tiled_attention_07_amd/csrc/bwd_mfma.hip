@@ -13,17 +13,20 @@
 //   dK/dV       one workgroup per (batch, kv head, tile of 32*NW keys); each
 //               wave keeps its 32 keys' K and V in registers and its dK^T, dV^T
 //               accumulators in registers, loops over the query heads of the
-//               group and the visible query tiles:
-//                 S  = Q K^T        (A = Q rows in LDS, B = K registers)
-//                 dV^T += dO^T P    (A = dO^T transposed in LDS, B = P)
-//                 dP = dO V^T       (A = dO rows in LDS, B = V registers)
-//                 dK^T += Q^T dS    (A = Q^T transposed in LDS, B = dS)
+//               group and the visible query tiles (one pipelined loop):
+//                 S  = Q K^T        (A = Q row chunks in LDS, B = K registers)
+//                 dP = dO V^T       (A = dO row chunks in LDS, B = V registers)
+//                 dV^T += dO^T P    (A = dO read transposed from LDS, B = P)
+//                 dK^T += Q^T dS    (A = Q read transposed from LDS, B = dS)
 //               GQA sums over the group inside the workgroup.
 //   dQ          one workgroup per (batch, query head, tile of 32*NW queries);
 //               the forward's layout (one query per lane):
 //                 S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T
 // The dQ kernel recomputes S and dP (7 tile products per score pair instead of
 // 5) in exchange for no atomic accumulation and no dQ workspace.
+// All staged tiles are row-major in LDS with the chunk swizzle of tile_io.hpp
+// and double buffered (one barrier per tile); operands whose reduction axis
+// runs along the tile rows come from the transposing LDS read.
 #include <type_traits>
 
 #include "common.hpp"
@@ -99,15 +102,11 @@ template <class T, int D, int BMQ, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BNK = NW * 32;  // keys per workgroup
-  using Tile = TileRegs<D, BMQ, NT>;
-  constexpr int RP = RowPitch<D>::value;
-  constexpr int CP = ColPitch<BMQ, Tile::R>::value;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BMQ * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[BMQ * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * CP];
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[D * CP];
-  __shared__ __attribute__((aligned(16))) float lse2s[BMQ];
-  __shared__ __attribute__((aligned(16))) float dsums[BMQ];
+  constexpr int TILE = BMQ * D;
+  using Tile = SwzTile<D, BMQ, NT>;
+  // Two buffers of (Q tile, dO tile), swizzled row-major, plus per-row LSE/D.
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) float rowstat[2][2][BMQ];  // [buf][lse2, D][row]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -145,124 +144,126 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(AttnArgs a) {
   const int k_last = min(k0 + BNK, a.Nk) - 1;
   const int i_lo = query_lo(a, k0), i_hi = query_hi(a, k_last);
   const int qt_lo = i_lo / BMQ;
-  const int qt_hi = (i_hi >= i_lo) ? i_hi / BMQ : qt_lo - 1;
+  const int n_qt = (i_hi >= i_lo) ? i_hi / BMQ - qt_lo + 1 : 0;
+  const int n_items = n_qt * a.G;  // (query head of the group, query tile) pairs
   const float c = a.scale_log2;
 
-  for (int g = 0; g < a.G; ++g) {
+  // Loader state for work item w: head hk*G + w / n_qt, tile qt_lo + w % n_qt.
+  Tile qt, dt;
+  qt.init(tid);
+  dt.init(tid);
+  float st_lse = INFINITY, st_d = 0.f;
+  auto load_item = [&](int w) {
+    const int g = w / n_qt, i0 = (qt_lo + w % n_qt) * BMQ;
     const int hq = hk * a.G + g;
-    const uint16_t* Qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh;
-    const uint16_t* dOp = static_cast<const uint16_t*>(a.dout) + b * a.o_sb + hq * a.o_sh;
-    const float* lsep = a.lse + ((int64_t)b * a.Hq + hq) * a.Nq;
-    const float* dsp = a.dsum + ((int64_t)b * a.Hq + hq) * a.Nq;
-
-    Tile qt, dt;
-    if (qt_lo <= qt_hi) {
-      qt.load(Qp, a.q_sn, qt_lo * BMQ, a.Nq, tid);
-      dt.load(dOp, a.o_sn, qt_lo * BMQ, a.Nq, tid);
+    qt.load(static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_sn, i0, a.Nq);
+    dt.load(static_cast<const uint16_t*>(a.dout) + b * a.o_sb + hq * a.o_sh, a.o_sn, i0, a.Nq);
+    if (tid < BMQ) {
+      const int i = i0 + tid;
+      const int64_t ri = ((int64_t)b * a.Hq + hq) * a.Nq + i;
+      st_lse = (i < a.Nq) ? lse_log2(a.lse[ri]) : INFINITY;
+      st_d = (i < a.Nq) ? a.dsum[ri] : 0.f;
     }
-    for (int t = qt_lo; t <= qt_hi; ++t) {
-      const int i0 = t * BMQ;
-      __syncthreads();
-      qt.template store_rows<RP>(Qs, tid);
-      qt.template store_cols<CP>(Qt, tid);
-      dt.template store_rows<RP>(dOs, tid);
-      dt.template store_cols<CP>(dOt, tid);
-      if (tid < BMQ) {
-        const int i = i0 + tid;
-        lse2s[tid] = (i < a.Nq) ? lse_log2(lsep[i]) : INFINITY;
-        dsums[tid] = (i < a.Nq) ? dsp[i] : 0.f;
-      }
-      __syncthreads();
-      if (t < qt_hi) {
-        qt.load(Qp, a.q_sn, i0 + BMQ, a.Nq, tid);
-        dt.load(dOp, a.o_sn, i0 + BMQ, a.Nq, tid);
-      }
+  };
+  auto store_item = [&](int buf) {
+    qt.store(smem + buf * 2 * TILE);
+    dt.store(smem + buf * 2 * TILE + TILE);
+    if (tid < BMQ) {
+      rowstat[buf][0][tid] = st_lse;
+      rowstat[buf][1][tid] = st_d;
+    }
+  };
 
-      // S = Q K^T; s[qb][r] is query i0 + 32*qb + 8*(r/4) + 4*hf + r%4.
-      f32x16 s[BMQ / 32];
+  if (n_items > 0) {
+    load_item(0);
+    store_item(0);
+  }
+  __syncthreads();
+  if (n_items > 1) load_item(1);
+
+  for (int w = 0; w < n_items; ++w) {
+    const int buf = w & 1;
+    const int i0 = (qt_lo + w % n_qt) * BMQ;
+    const uint16_t* Qs = smem + buf * 2 * TILE;
+    const uint16_t* dOs = Qs + TILE;
+    const float* lse2s = rowstat[buf][0];
+    const float* dsums = rowstat[buf][1];
+
+    // S = Q K^T; s[qb][r] is query i0 + 32*qb + 8*(r/4) + 4*hf + r%4.
+    f32x16 s[BMQ / 32];
 #pragma unroll
-      for (int qb = 0; qb < BMQ / 32; ++qb) s[qb] = f32x16{};
+    for (int qb = 0; qb < BMQ / 32; ++qb) s[qb] = f32x16{};
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
+    for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
-        for (int qb = 0; qb < BMQ / 32; ++qb)
-          s[qb] = T::mfma(lds_row8(Qs + (32 * qb + l32) * RP + 16 * st + 8 * hf), kf[st], s[qb]);
-      }
-      // Mask: exact per-element test only where the tile pair is not fully visible.
-      const int i_end = min(i0 + BMQ, a.Nq) - 1;
-      const bool full = (key_lo(a, i_end) <= k0) && (key_hi(a, i0) >= k_last);
-      if (!full) {
+      for (int qb = 0; qb < BMQ / 32; ++qb)
+        s[qb] = T::mfma(swz_chunk<D>(Qs, 32 * qb + l32, 2 * st + hf), kf[st], s[qb]);
+    }
+    // dP = dO V^T (independent of S, issued before the softmax math).
+    f32x16 dp[BMQ / 32];
 #pragma unroll
-        for (int qb = 0; qb < BMQ / 32; ++qb) {
+    for (int qb = 0; qb < BMQ / 32; ++qb) dp[qb] = f32x16{};
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = i0 + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key < key_lo(a, i) || key > key_hi(a, i)) s[qb][r] = -INFINITY;
-          }
-        }
-      }
-      // P = exp2(s*c - lse2) and dV^T += dO^T P.
-      u32x4 pf[BMQ / 16];
-      float p[BMQ / 32][16];
+    for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+      for (int qb = 0; qb < BMQ / 32; ++qb)
+        dp[qb] = T::mfma(swz_chunk<D>(dOs, 32 * qb + l32, 2 * st + hf), vf[st], dp[qb]);
+    }
+    // Mask: exact per-element test only where the tile pair is not fully visible.
+    const int i_end = min(i0 + BMQ, a.Nq) - 1;
+    const bool full = (key_lo(a, i_end) <= k0) && (key_hi(a, i0) >= k_last);
+    if (!full) {
 #pragma unroll
       for (int qb = 0; qb < BMQ / 32; ++qb) {
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 32 * qb + 8 * g4 + 4 * hf);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) p[qb][4 * g4 + e] = fast_exp2(fmaf(s[qb][4 * g4 + e], c, -l4[e]));
+        for (int r = 0; r < 16; ++r) {
+          const int i = i0 + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key < key_lo(a, i) || key > key_hi(a, i)) s[qb][r] = -INFINITY;
         }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const float* pp = &p[qb][8 * tt];
-          pf[2 * qb + tt] = u32x4{T::pack(pp[0], pp[1]), T::pack(pp[2], pp[3]), T::pack(pp[4], pp[5]),
-                                  T::pack(pp[6], pp[7])};
-        }
-      }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int si = 0; si < BMQ / 16; ++si)
-          dva[db] = T::mfma(lds_col8(dOt + (32 * db + l32) * CP + 16 * si + 4 * hf), pf[si], dva[db]);
-      }
-      // dP = dO V^T.
-      f32x16 dp[BMQ / 32];
-#pragma unroll
-      for (int qb = 0; qb < BMQ / 32; ++qb) dp[qb] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-#pragma unroll
-        for (int qb = 0; qb < BMQ / 32; ++qb)
-          dp[qb] = T::mfma(lds_row8(dOs + (32 * qb + l32) * RP + 16 * st + 8 * hf), vf[st], dp[qb]);
-      }
-      // dS = P * (dP - D) and dK^T += Q^T dS.
-      u32x4 dsf[BMQ / 16];
-#pragma unroll
-      for (int qb = 0; qb < BMQ / 32; ++qb) {
-        float ds[16];
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsums + 32 * qb + 8 * g4 + 4 * hf);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ds[4 * g4 + e] = p[qb][4 * g4 + e] * (dp[qb][4 * g4 + e] - d4[e]);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const float* q8 = &ds[8 * tt];
-          dsf[2 * qb + tt] = u32x4{T::pack(q8[0], q8[1]), T::pack(q8[2], q8[3]), T::pack(q8[4], q8[5]),
-                                   T::pack(q8[6], q8[7])};
-        }
-      }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int si = 0; si < BMQ / 16; ++si)
-          dka[db] = T::mfma(lds_col8(Qt + (32 * db + l32) * CP + 16 * si + 4 * hf), dsf[si], dka[db]);
       }
     }
+    // P = exp2(s*c - lse2) and dS = P * (dP - D), both as B operands.
+    u32x4 pf[BMQ / 16], dsf[BMQ / 16];
+#pragma unroll
+    for (int qb = 0; qb < BMQ / 32; ++qb) {
+      float p[16], ds[16];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 32 * qb + 8 * g4 + 4 * hf);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsums + 32 * qb + 8 * g4 + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          p[r] = fast_exp2(fmaf(s[qb][r], c, -l4[e]));
+          ds[r] = p[r] * (dp[qb][r] - d4[e]);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const float* pp = &p[8 * tt];
+        const float* qq = &ds[8 * tt];
+        pf[2 * qb + tt] = u32x4{T::pack(pp[0], pp[1]), T::pack(pp[2], pp[3]), T::pack(pp[4], pp[5]),
+                                T::pack(pp[6], pp[7])};
+        dsf[2 * qb + tt] = u32x4{T::pack(qq[0], qq[1]), T::pack(qq[2], qq[3]), T::pack(qq[4], qq[5]),
+                                 T::pack(qq[6], qq[7])};
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, operands read transposed from the tiles.
+#pragma unroll
+    for (int si = 0; si < BMQ / 16; ++si) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        dva[db] = T::mfma(swz_tr_operand<D>(dOs, si, db, lane), pf[si], dva[db]);
+        dka[db] = T::mfma(swz_tr_operand<D>(Qs, si, db, lane), dsf[si], dka[db]);
+      }
+    }
+
+    if (w + 1 < n_items) store_item(buf ^ 1);
+    __syncthreads();
+    if (w + 2 < n_items) load_item(w + 2);
   }
 
-  // Store dK = scale * dK^T^T and dV: lane holds d rows 32*db + 8*g4 + 4*hf + 0..3.
+  // Store dK = scale * dK and dV: lane holds d rows 32*db + 8*g4 + 4*hf + 0..3.
   if (key < a.Nk) {
     uint16_t* dkp = static_cast<uint16_t*>(a.dk) + b * a.k_sb + hk * a.k_sh + (int64_t)key * a.k_sn;
     uint16_t* dvp = static_cast<uint16_t*>(a.dv) + b * a.v_sb + hk * a.v_sh + (int64_t)key * a.v_sn;
@@ -289,12 +290,9 @@ template <class T, int D, int BN, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
-  using Tile = TileRegs<D, BN, NT>;
-  constexpr int RP = RowPitch<D>::value;
-  constexpr int CP = ColPitch<BN, Tile::R>::value;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * RP];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * CP];
+  constexpr int TILE = BN * D;
+  using Tile = SwzTile<D, BN, NT>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];  // [buf][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -344,21 +342,24 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
   for (int db = 0; db < D / 32; ++db) dqa[db] = f32x16{};
 
   Tile kt, vt;
+  kt.init(tid);
+  vt.init(tid);
   if (t_lo <= t_hi) {
-    kt.load(Kp, a.k_sn, t_lo * BN, a.Nk, tid);
-    vt.load(Vp, a.v_sn, t_lo * BN, a.Nk, tid);
+    kt.load(Kp, a.k_sn, t_lo * BN, a.Nk);
+    vt.load(Vp, a.v_sn, t_lo * BN, a.Nk);
+    kt.store(smem);
+    vt.store(smem + TILE);
+  }
+  __syncthreads();
+  if (t_lo + 1 <= t_hi) {
+    kt.load(Kp, a.k_sn, (t_lo + 1) * BN, a.Nk);
+    vt.load(Vp, a.v_sn, (t_lo + 1) * BN, a.Nk);
   }
   for (int t = t_lo; t <= t_hi; ++t) {
     const int j0 = t * BN;
-    __syncthreads();
-    kt.template store_rows<RP>(Ks, tid);
-    kt.template store_cols<CP>(Kt, tid);
-    vt.template store_rows<RP>(Vs, tid);
-    __syncthreads();
-    if (t < t_hi) {
-      kt.load(Kp, a.k_sn, j0 + BN, a.Nk, tid);
-      vt.load(Vp, a.v_sn, j0 + BN, a.Nk, tid);
-    }
+    const int buf = (t - t_lo) & 1;
+    const uint16_t* Ks = smem + buf * 2 * TILE;
+    const uint16_t* Vs = Ks + TILE;
     // S^T = K Q^T and dP^T = V dO^T; element [kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
     f32x16 s[BN / 32], dp[BN / 32];
 #pragma unroll
@@ -367,8 +368,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
     for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
-        s[kb] = T::mfma(lds_row8(Ks + (32 * kb + l32) * RP + 16 * st + 8 * hf), qf[st], s[kb]);
-        dp[kb] = T::mfma(lds_row8(Vs + (32 * kb + l32) * RP + 16 * st + 8 * hf), df[st], dp[kb]);
+        s[kb] = T::mfma(swz_chunk<D>(Ks, 32 * kb + l32, 2 * st + hf), qf[st], s[kb]);
+        dp[kb] = T::mfma(swz_chunk<D>(Vs, 32 * kb + l32, 2 * st + hf), df[st], dp[kb]);
       }
     }
     const bool full = (j0 >= lo_max) && (j0 + BN - 1 <= hi_min);
@@ -377,8 +378,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
       for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key < lo_i || key > hi_i) s[kb][r] = -INFINITY;
+          const int kk = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (kk < lo_i || kk > hi_i) s[kb][r] = -INFINITY;
         }
       }
     }
@@ -400,10 +401,20 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int si = 0; si < BN / 16; ++si) {
 #pragma unroll
-      for (int si = 0; si < BN / 16; ++si)
-        dqa[db] = T::mfma(lds_col8(Kt + (32 * db + l32) * CP + 16 * si + 4 * hf), dsf[si], dqa[db]);
+      for (int db = 0; db < D / 32; ++db)
+        dqa[db] = T::mfma(swz_tr_operand<D>(Ks, si, db, lane), dsf[si], dqa[db]);
+    }
+
+    if (t < t_hi) {
+      kt.store(smem + (buf ^ 1) * 2 * TILE);
+      vt.store(smem + (buf ^ 1) * 2 * TILE + TILE);
+    }
+    __syncthreads();
+    if (t + 2 <= t_hi) {
+      kt.load(Kp, a.k_sn, j0 + 2 * BN, a.Nk);
+      vt.load(Vp, a.v_sn, j0 + 2 * BN, a.Nk);
     }
   }
 
