@@ -36,14 +36,20 @@
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// D_i = sum_c dout[i, c] * o[i, c]   (any dtype; 16 lanes per row)
+// Row statistics for the backward kernels, one float each per (b, h, row) in
+// arrays padded to Nq_pad = ceil(Nq / 128) * 128 rows:
+//   dsum[row] = D_i = sum_c dout[i, c] * o[i, c]    (0 for padding rows)
+//   lse2[row] = LSE_i * log2(e)                      (+inf for padding rows and
+//               for rows that see no key, so exp2(s*c - lse2) is exactly 0)
+// Any dtype; 16 lanes per row.
 // ---------------------------------------------------------------------------
 template <int ELT>  // element bytes: 4 (fp32) or 2 (fp16/bf16)
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a) {
   constexpr int EPC = 16 / ELT;  // elements per 16-byte chunk
+  const int nq_pad = (a.Nq + 127) / 128 * 128;
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
-  const int64_t rows = (int64_t)a.B * a.Nq * a.Hq;
+  const int64_t rows = (int64_t)a.B * nq_pad * a.Hq;
   // fp32 inputs accumulate in float64 (exact products); 16-bit inputs in fp32.
   using Acc = typename std::conditional<ELT == 4, double, float>::type;
   Acc acc = 0;
@@ -51,35 +57,46 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a) {
   if (row < rows) {
     h = (int)(row % a.Hq);
     const int64_t t = row / a.Hq;
-    i = (int)(t % a.Nq);
-    b = (int)(t / a.Nq);
-    const char* dop = static_cast<const char*>(a.dout) +
-                      (b * a.o_sb + (int64_t)i * a.o_sn + h * a.o_sh) * ELT;
-    const char* op = static_cast<const char*>(a.o) + (b * a.o_sb + (int64_t)i * a.o_sn + h * a.o_sh) * ELT;
-    for (int cc = sub; cc * EPC < a.D; cc += 16) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(dop + cc * 16);
-      const u32x4 y = *reinterpret_cast<const u32x4*>(op + cc * 16);
+    i = (int)(t % nq_pad);
+    b = (int)(t / nq_pad);
+    if (i < a.Nq) {
+      const int64_t base = (b * a.o_sb + (int64_t)i * a.o_sn + h * a.o_sh) * ELT;
+      const char* dop = static_cast<const char*>(a.dout) + base;
+      const char* op = static_cast<const char*>(a.o) + base;
+      for (int cc = sub; cc * EPC < a.D; cc += 16) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(dop + cc * 16);
+        const u32x4 y = *reinterpret_cast<const u32x4*>(op + cc * 16);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if constexpr (ELT == 4) {
-          acc = fma((double)__uint_as_float(x[w]), (double)__uint_as_float(y[w]), acc);
-        } else if (a.dtype == kBF16) {
-          acc = fmaf(BF16::to_f32(x[w] & 0xffffu), BF16::to_f32(y[w] & 0xffffu), acc);
-          acc = fmaf(BF16::to_f32(x[w] >> 16), BF16::to_f32(y[w] >> 16), acc);
-        } else {
-          acc = fmaf(F16::to_f32(x[w] & 0xffffu), F16::to_f32(y[w] & 0xffffu), acc);
-          acc = fmaf(F16::to_f32(x[w] >> 16), F16::to_f32(y[w] >> 16), acc);
+        for (int w = 0; w < 4; ++w) {
+          if constexpr (ELT == 4) {
+            acc = fma((double)__uint_as_float(x[w]), (double)__uint_as_float(y[w]), acc);
+          } else if (a.dtype == kBF16) {
+            acc = fmaf(BF16::to_f32(x[w] & 0xffffu), BF16::to_f32(y[w] & 0xffffu), acc);
+            acc = fmaf(BF16::to_f32(x[w] >> 16), BF16::to_f32(y[w] >> 16), acc);
+          } else {
+            acc = fmaf(F16::to_f32(x[w] & 0xffffu), F16::to_f32(y[w] & 0xffffu), acc);
+            acc = fmaf(F16::to_f32(x[w] >> 16), F16::to_f32(y[w] >> 16), acc);
+          }
         }
       }
     }
   }
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-  if (row < rows && sub == 0) a.dsum[((int64_t)b * a.Hq + h) * a.Nq + i] = (float)acc;
+  if (row < rows && sub == 0) {
+    const int64_t o = ((int64_t)b * a.Hq + h) * nq_pad + i;
+    a.dsum[o] = (float)acc;
+    float l2 = INFINITY;
+    if (i < a.Nq) {
+      const float L = a.lse[((int64_t)b * a.Hq + h) * a.Nq + i];
+      if (L != -INFINITY) l2 = L * kLog2e;
+    }
+    a.lse2[o] = l2;
+  }
 }
 
 hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * a.Nq * a.Hq;
+  const int64_t rows = (int64_t)a.B * ((a.Nq + 127) / 128 * 128) * a.Hq;
   if (rows == 0) return hipSuccess;
   const unsigned grid = (unsigned)((rows + 15) / 16);
   if (a.dtype == kF32)
@@ -89,136 +106,128 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// log2-domain LSE of a query row; a row that sees no key (LSE = -inf) gets +inf
-// so that every recomputed probability exp2(s*c - lse2) of it is exactly 0.
-__device__ __forceinline__ float lse_log2(float lse) {
-  return (lse == -INFINITY) ? INFINITY : lse * kLog2e;
-}
+// Launch configuration (tuned on MI355X; overridable at build time).
+#ifndef FA_DKDV_BMQ
+#define FA_DKDV_BMQ 64  // queries per dK/dV iteration
+#endif
+#ifndef FA_DKDV_NW
+#define FA_DKDV_NW 4  // waves per dK/dV workgroup (32 keys each)
+#endif
+#ifndef FA_DKDV_WPE
+#define FA_DKDV_WPE 1
+#endif
+#ifndef FA_DQ_BN
+#define FA_DQ_BN 64  // keys per dQ iteration
+#endif
+#ifndef FA_DQ_NW
+#define FA_DQ_NW 8  // waves per dQ workgroup (32 queries each)
+#endif
+#ifndef FA_DQ_WPE
+#define FA_DQ_WPE 2
+#endif
+
+// Per-lane LDS byte offsets of a swizzled D-wide tile (tile_io.hpp):
+// row chunks for an operand whose lanes run along the rows (row l32 of each
+// 32-row block, chunk 2*st + hf), and the transposing reads for an operand
+// whose reduction axis runs along the rows (16-row step 0, column block db,
+// lower/upper 8 rows).  Row-block, step and buffer offsets are immediates.
+template <int D>
+struct SwzOffsets {
+  int chunk[D / 16];
+  int tr[D / 32][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) chunk[st] = Swz<D>::off(l32, 2 * st + hf);
+    const int G = lane >> 4, j = lane & 15;
+    const int vhf = G >> 1, gsub = G & 1, ep = j >> 2, q = j & 3;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int cc = 4 * db + 2 * gsub + (q >> 1);
+      tr[db][0] = Swz<D>::off(4 * vhf + ep, cc) + 8 * (q & 1);
+      tr[db][1] = Swz<D>::off(8 + 4 * vhf + ep, cc) + 8 * (q & 1);
+    }
+  }
+  // Row chunk operand at row-block rb (32 rows) of the tile at `tile`.
+  __device__ __forceinline__ u32x4 row_chunk(const char* tile, int rb, int st) const {
+    return *reinterpret_cast<const u32x4*>(tile + rb * 32 * 2 * D + chunk[st]);
+  }
+  // Transposed operand for 16-row step si and column block db.
+  __device__ __forceinline__ u32x4 tr_operand(const char* tile, int si, int db) const {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + si * 16 * 2 * D + tr[db][0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + si * 16 * 2 * D + tr[db][1]));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+};
 
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
 template <class T, int D, int BMQ, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int BNK = NW * 32;  // keys per workgroup
-  constexpr int TILE = BMQ * D;
-  using Tile = SwzTile<D, BMQ, NT>;
-  // Two buffers of (Q tile, dO tile), swizzled row-major, plus per-row LSE/D.
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
-  __shared__ __attribute__((aligned(16))) float rowstat[2][2][BMQ];  // [buf][lse2, D][row]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hf = lane >> 5;
-
-  const int n_kt = (a.Nk + BNK - 1) / BNK;
-  // Under a causal mask the first key tiles see the most queries: run them first.
-  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_kt, 1, false, a.xcd_remap);
-  const int b = it.unit / a.Hkv, hk = it.unit % a.Hkv;
-  const int k0 = it.tile * BNK;
-  const int key = k0 + wave * 32 + l32;  // this lane's key (accumulator column)
-
-  const uint16_t* Kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + hk * a.k_sh;
-  const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + hk * a.v_sh;
-
-  // K and V as B operands (lane: key, d = 16*st + 8*hf + 0..7).
+struct DkdvCtx {
+  static constexpr int TILE = BMQ * D;
+  uint16_t* smem;  // [buf][Q tile, dO tile]
+  float* rstat;    // [buf][lse2[BMQ], dsum[BMQ]]
+  const AttnArgs* a;
+  int b, hk, k0, k_last, key, qt_lo, n_qt, n_items, wave, lane, hf, nq_pad;
+  float c;
   u32x4 kf[D / 16], vf[D / 16];
-  if (key < a.Nk) {
-    const uint16_t* kr = Kp + (int64_t)key * a.k_sn + 8 * hf;
-    const uint16_t* vr = Vp + (int64_t)key * a.v_sn + 8 * hf;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      kf[st] = *reinterpret_cast<const u32x4*>(kr + 16 * st);
-      vf[st] = *reinterpret_cast<const u32x4*>(vr + 16 * st);
-    }
-  } else {
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) kf[st] = vf[st] = u32x4{0u, 0u, 0u, 0u};
-  }
-
   f32x16 dka[D / 32], dva[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) dka[db] = dva[db] = f32x16{};
+  SwzOffsets<D> off;
+  DmaTile<D, BMQ, NW> qd, dd;
 
-  const int k_last = min(k0 + BNK, a.Nk) - 1;
-  const int i_lo = query_lo(a, k0), i_hi = query_hi(a, k_last);
-  const int qt_lo = i_lo / BMQ;
-  const int n_qt = (i_hi >= i_lo) ? i_hi / BMQ - qt_lo + 1 : 0;
-  const int n_items = n_qt * a.G;  // (query head of the group, query tile) pairs
-  const float c = a.scale_log2;
-
-  // Loader state for work item w: head hk*G + w / n_qt, tile qt_lo + w % n_qt.
-  Tile qt, dt;
-  qt.init(tid);
-  dt.init(tid);
-  float st_lse = INFINITY, st_d = 0.f;
-  auto load_item = [&](int w) {
+  // Start the loads of work item w (query head of the group, query tile).
+  template <int BUF>
+  __device__ __forceinline__ void issue(int w) {
     const int g = w / n_qt, i0 = (qt_lo + w % n_qt) * BMQ;
-    const int hq = hk * a.G + g;
-    qt.load(static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh, a.q_sn, i0, a.Nq);
-    dt.load(static_cast<const uint16_t*>(a.dout) + b * a.o_sb + hq * a.o_sh, a.o_sn, i0, a.Nq);
-    if (tid < BMQ) {
-      const int i = i0 + tid;
-      const int64_t ri = ((int64_t)b * a.Hq + hq) * a.Nq + i;
-      st_lse = (i < a.Nq) ? lse_log2(a.lse[ri]) : INFINITY;
-      st_d = (i < a.Nq) ? a.dsum[ri] : 0.f;
+    const int hq = hk * a->G + g;
+    qd.issue(static_cast<const uint16_t*>(a->q) + b * a->q_sb + hq * a->q_sh, a->q_sn, i0, a->Nq,
+             smem + BUF * 2 * TILE, wave);
+    dd.issue(static_cast<const uint16_t*>(a->dout) + b * a->o_sb + hq * a->o_sh, a->o_sn, i0, a->Nq,
+             smem + BUF * 2 * TILE + TILE, wave);
+    if (wave == 0) {
+      const int64_t ro = ((int64_t)b * a->Hq + hq) * nq_pad + i0;
+      if (lane < BMQ / 4) {
+        // 4 floats per lane: lse2 then dsum rows of this tile (padded arrays).
+        dma16(a->lse2 + ro + 4 * lane, reinterpret_cast<uint16_t*>(rstat + BUF * 2 * BMQ));
+      } else if (lane < BMQ / 2) {
+        dma16(a->dsum + ro + 4 * (lane - BMQ / 4), reinterpret_cast<uint16_t*>(rstat + BUF * 2 * BMQ));
+      }
     }
-  };
-  auto store_item = [&](int buf) {
-    qt.store(smem + buf * 2 * TILE);
-    dt.store(smem + buf * 2 * TILE + TILE);
-    if (tid < BMQ) {
-      rowstat[buf][0][tid] = st_lse;
-      rowstat[buf][1][tid] = st_d;
-    }
-  };
-
-  if (n_items > 0) {
-    load_item(0);
-    store_item(0);
   }
-  __syncthreads();
-  if (n_items > 1) load_item(1);
 
-  for (int w = 0; w < n_items; ++w) {
-    const int buf = w & 1;
+  template <int BUF>
+  __device__ __forceinline__ void step(int w) {
+    const char* Qs = reinterpret_cast<const char*>(smem + BUF * 2 * TILE);
+    const char* dOs = Qs + TILE * 2;
+    const float* lse2s = rstat + BUF * 2 * BMQ;
+    const float* dsums = lse2s + BMQ;
     const int i0 = (qt_lo + w % n_qt) * BMQ;
-    const uint16_t* Qs = smem + buf * 2 * TILE;
-    const uint16_t* dOs = Qs + TILE;
-    const float* lse2s = rowstat[buf][0];
-    const float* dsums = rowstat[buf][1];
+    if (w + 1 < n_items) issue<1 - BUF>(w + 1);
 
-    // S = Q K^T; s[qb][r] is query i0 + 32*qb + 8*(r/4) + 4*hf + r%4.
-    f32x16 s[BMQ / 32];
+    // S = Q K^T and dP = dO V^T; [qb][r] is query i0 + 32*qb + 8*(r/4) + 4*hf + r%4.
+    f32x16 s[BMQ / 32], dp[BMQ / 32];
 #pragma unroll
-    for (int qb = 0; qb < BMQ / 32; ++qb) s[qb] = f32x16{};
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-#pragma unroll
-      for (int qb = 0; qb < BMQ / 32; ++qb)
-        s[qb] = T::mfma(swz_chunk<D>(Qs, 32 * qb + l32, 2 * st + hf), kf[st], s[qb]);
-    }
-    // dP = dO V^T (independent of S, issued before the softmax math).
-    f32x16 dp[BMQ / 32];
-#pragma unroll
-    for (int qb = 0; qb < BMQ / 32; ++qb) dp[qb] = f32x16{};
+    for (int qb = 0; qb < BMQ / 32; ++qb) s[qb] = dp[qb] = f32x16{};
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
-      for (int qb = 0; qb < BMQ / 32; ++qb)
-        dp[qb] = T::mfma(swz_chunk<D>(dOs, 32 * qb + l32, 2 * st + hf), vf[st], dp[qb]);
+      for (int qb = 0; qb < BMQ / 32; ++qb) {
+        s[qb] = T::mfma(off.row_chunk(Qs, qb, st), kf[st], s[qb]);
+        dp[qb] = T::mfma(off.row_chunk(dOs, qb, st), vf[st], dp[qb]);
+      }
     }
     // Mask: exact per-element test only where the tile pair is not fully visible.
-    const int i_end = min(i0 + BMQ, a.Nq) - 1;
-    const bool full = (key_lo(a, i_end) <= k0) && (key_hi(a, i0) >= k_last);
+    const int i_end = min(i0 + BMQ, a->Nq) - 1;
+    const bool full = (key_lo(*a, i_end) <= k0) && (key_hi(*a, i0) >= k_last);
     if (!full) {
 #pragma unroll
       for (int qb = 0; qb < BMQ / 32; ++qb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int i = i0 + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key < key_lo(a, i) || key > key_hi(a, i)) s[qb][r] = -INFINITY;
+          if (key < key_lo(*a, i) || key > key_hi(*a, i)) s[qb][r] = -INFINITY;
         }
       }
     }
@@ -253,20 +262,88 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(AttnArgs a) {
     for (int si = 0; si < BMQ / 16; ++si) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        dva[db] = T::mfma(swz_tr_operand<D>(dOs, si, db, lane), pf[si], dva[db]);
-        dka[db] = T::mfma(swz_tr_operand<D>(Qs, si, db, lane), dsf[si], dka[db]);
+        dva[db] = T::mfma(off.tr_operand(dOs, si, db), pf[si], dva[db]);
+        dka[db] = T::mfma(off.tr_operand(Qs, si, db), dsf[si], dka[db]);
       }
     }
-
-    if (w + 1 < n_items) store_item(buf ^ 1);
+    wait_all_loads();
     __syncthreads();
-    if (w + 2 < n_items) load_item(w + 2);
   }
+};
+
+template <class T, int D, int BMQ, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DKDV_WPE, FA_DKDV_WPE))) void bwd_dkdv_kernel(AttnArgs a) {
+  constexpr int BNK = NW * 32;  // keys per workgroup
+  using Ctx = DkdvCtx<T, D, BMQ, NW>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * Ctx::TILE];
+  __shared__ __attribute__((aligned(16))) float rstat[2 * 2 * BMQ];
+  static_assert(2 * 2 * Ctx::TILE * 2 <= 65536, "LDS offsets must fit the 16-bit immediate");
+  static_assert(BMQ <= 128 && 128 % BMQ == 0, "row statistics are padded to 128 rows");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int n_kt = (a.Nk + BNK - 1) / BNK;
+  // Under a causal mask the first key tiles see the most queries: run them first.
+  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_kt, 1, false, a.xcd_remap);
+
+  Ctx x;
+  x.smem = smem;
+  x.rstat = rstat;
+  x.a = &a;
+  x.b = it.unit / a.Hkv;
+  x.hk = it.unit % a.Hkv;
+  x.k0 = it.tile * BNK;
+  x.key = x.k0 + wave * 32 + l32;  // this lane's key (accumulator column)
+  x.wave = wave;
+  x.lane = lane;
+  x.hf = hf;
+  x.c = a.scale_log2;
+  x.nq_pad = (a.Nq + 127) / 128 * 128;
+
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.k) + x.b * a.k_sb + x.hk * a.k_sh;
+  const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + x.b * a.v_sb + x.hk * a.v_sh;
+  // K and V as B operands (lane: key, d = 16*st + 8*hf + 0..7).
+  if (x.key < a.Nk) {
+    const uint16_t* kr = Kp + (int64_t)x.key * a.k_sn + 8 * hf;
+    const uint16_t* vr = Vp + (int64_t)x.key * a.v_sn + 8 * hf;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      x.kf[st] = *reinterpret_cast<const u32x4*>(kr + 16 * st);
+      x.vf[st] = *reinterpret_cast<const u32x4*>(vr + 16 * st);
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) x.kf[st] = x.vf[st] = u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) x.dka[db] = x.dva[db] = f32x16{};
+
+  x.k_last = min(x.k0 + BNK, a.Nk) - 1;
+  const int i_lo = query_lo(a, x.k0), i_hi = query_hi(a, x.k_last);
+  x.qt_lo = i_lo / BMQ;
+  x.n_qt = (i_hi >= i_lo) ? i_hi / BMQ - x.qt_lo + 1 : 0;
+  x.n_items = x.n_qt * a.G;  // (query head of the group, query tile) pairs
+  x.off.init(lane);
+  x.qd.init(wave, lane, a.q_sn);
+  x.dd.init(wave, lane, a.o_sn);
+
+  if (x.n_items > 0) {
+    x.template issue<0>(0);
+    wait_all_loads();
+  }
+  __syncthreads();
+  int w = 0;
+  for (; w + 1 < x.n_items; w += 2) {
+    x.template step<0>(w);
+    x.template step<1>(w + 1);
+  }
+  if (w < x.n_items) x.template step<0>(w);
 
   // Store dK = scale * dK and dV: lane holds d rows 32*db + 8*g4 + 4*hf + 0..3.
-  if (key < a.Nk) {
-    uint16_t* dkp = static_cast<uint16_t*>(a.dk) + b * a.k_sb + hk * a.k_sh + (int64_t)key * a.k_sn;
-    uint16_t* dvp = static_cast<uint16_t*>(a.dv) + b * a.v_sb + hk * a.v_sh + (int64_t)key * a.v_sn;
+  if (x.key < a.Nk) {
+    uint16_t* dkp = static_cast<uint16_t*>(a.dk) + x.b * a.k_sb + x.hk * a.k_sh + (int64_t)x.key * a.k_sn;
+    uint16_t* dvp = static_cast<uint16_t*>(a.dv) + x.b * a.v_sb + x.hk * a.v_sh + (int64_t)x.key * a.v_sn;
     const float sc = a.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -274,10 +351,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(AttnArgs a) {
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * db + 8 * g4 + 4 * hf;
         *reinterpret_cast<u32x2*>(dkp + d0) =
-            u32x2{T::pack(dka[db][4 * g4] * sc, dka[db][4 * g4 + 1] * sc),
-                  T::pack(dka[db][4 * g4 + 2] * sc, dka[db][4 * g4 + 3] * sc)};
+            u32x2{T::pack(x.dka[db][4 * g4] * sc, x.dka[db][4 * g4 + 1] * sc),
+                  T::pack(x.dka[db][4 * g4 + 2] * sc, x.dka[db][4 * g4 + 3] * sc)};
         *reinterpret_cast<u32x2*>(dvp + d0) =
-            u32x2{T::pack(dva[db][4 * g4], dva[db][4 * g4 + 1]), T::pack(dva[db][4 * g4 + 2], dva[db][4 * g4 + 3])};
+            u32x2{T::pack(x.dva[db][4 * g4], x.dva[db][4 * g4 + 1]),
+                  T::pack(x.dva[db][4 * g4 + 2], x.dva[db][4 * g4 + 3])};
       }
     }
   }
@@ -287,79 +365,28 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(AttnArgs a) {
 // dQ
 // ---------------------------------------------------------------------------
 template <class T, int D, int BN, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int BM = NW * 32;
-  constexpr int TILE = BN * D;
-  using Tile = SwzTile<D, BN, NT>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];  // [buf][K, V]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hf = lane >> 5;
-
-  const int n_qt = (a.Nq + BM - 1) / BM;
-  const bool heavy_last = (a.causal || a.wr >= 0) && a.wl < 0;
-  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_qt, a.G, heavy_last, a.xcd_remap);
-  const int b = it.unit / a.Hkv, hk = it.unit % a.Hkv;
-  const int hq = hk * a.G + it.sub;
-  const int q0 = it.tile * BM;
-  const int qrow = q0 + wave * 32 + l32;
-
-  const uint16_t* Qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh;
-  const uint16_t* dOp = static_cast<const uint16_t*>(a.dout) + b * a.o_sb + hq * a.o_sh;
-  const uint16_t* Kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + hk * a.k_sh;
-  const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + hk * a.v_sh;
-
+struct DqCtx {
+  static constexpr int TILE = BN * D;
+  uint16_t* smem;  // [buf][K tile, V tile]
+  const uint16_t* Kp;
+  const uint16_t* Vp;
+  int64_t k_sn, v_sn;
+  int Nk, t_hi, lo_i, hi_i, lo_max, hi_min, wave, hf;
+  float c, lse2, dsum;
   u32x4 qf[D / 16], df[D / 16];
-  float lse2 = INFINITY, dsum = 0.f;
-  if (qrow < a.Nq) {
-    const uint16_t* qr = Qp + (int64_t)qrow * a.q_sn + 8 * hf;
-    const uint16_t* dr = dOp + (int64_t)qrow * a.o_sn + 8 * hf;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      qf[st] = *reinterpret_cast<const u32x4*>(qr + 16 * st);
-      df[st] = *reinterpret_cast<const u32x4*>(dr + 16 * st);
-    }
-    const int64_t ri = ((int64_t)b * a.Hq + hq) * a.Nq + qrow;
-    lse2 = lse_log2(a.lse[ri]);
-    dsum = a.dsum[ri];
-  } else {
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) qf[st] = df[st] = u32x4{0u, 0u, 0u, 0u};
-  }
-
-  const int lo_i = key_lo(a, qrow), hi_i = key_hi(a, qrow);
-  const int q_last = min(q0 + BM, a.Nq) - 1;
-  const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
-  const int lo_max = key_lo(a, q_last), hi_min = key_hi(a, q0);
-  const int t_lo = kv_lo / BN;
-  const int t_hi = (kv_hi >= kv_lo) ? kv_hi / BN : t_lo - 1;
-  const float c = a.scale_log2;
-
   f32x16 dqa[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) dqa[db] = f32x16{};
+  SwzOffsets<D> off;
+  DmaTile<D, BN, NW> kd, vd;
 
-  Tile kt, vt;
-  kt.init(tid);
-  vt.init(tid);
-  if (t_lo <= t_hi) {
-    kt.load(Kp, a.k_sn, t_lo * BN, a.Nk);
-    vt.load(Vp, a.v_sn, t_lo * BN, a.Nk);
-    kt.store(smem);
-    vt.store(smem + TILE);
-  }
-  __syncthreads();
-  if (t_lo + 1 <= t_hi) {
-    kt.load(Kp, a.k_sn, (t_lo + 1) * BN, a.Nk);
-    vt.load(Vp, a.v_sn, (t_lo + 1) * BN, a.Nk);
-  }
-  for (int t = t_lo; t <= t_hi; ++t) {
+  template <int BUF>
+  __device__ __forceinline__ void step(int t) {
+    const char* Ks = reinterpret_cast<const char*>(smem + BUF * 2 * TILE);
+    const char* Vs = Ks + TILE * 2;
     const int j0 = t * BN;
-    const int buf = (t - t_lo) & 1;
-    const uint16_t* Ks = smem + buf * 2 * TILE;
-    const uint16_t* Vs = Ks + TILE;
+    if (t < t_hi) {
+      kd.issue(Kp, k_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE, wave);
+      vd.issue(Vp, v_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE + TILE, wave);
+    }
     // S^T = K Q^T and dP^T = V dO^T; element [kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
     f32x16 s[BN / 32], dp[BN / 32];
 #pragma unroll
@@ -368,8 +395,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
     for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
-        s[kb] = T::mfma(swz_chunk<D>(Ks, 32 * kb + l32, 2 * st + hf), qf[st], s[kb]);
-        dp[kb] = T::mfma(swz_chunk<D>(Vs, 32 * kb + l32, 2 * st + hf), df[st], dp[kb]);
+        s[kb] = T::mfma(off.row_chunk(Ks, kb, st), qf[st], s[kb]);
+        dp[kb] = T::mfma(off.row_chunk(Vs, kb, st), df[st], dp[kb]);
       }
     }
     const bool full = (j0 >= lo_max) && (j0 + BN - 1 <= hi_min);
@@ -403,20 +430,87 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
     for (int si = 0; si < BN / 16; ++si) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        dqa[db] = T::mfma(swz_tr_operand<D>(Ks, si, db, lane), dsf[si], dqa[db]);
+      for (int db = 0; db < D / 32; ++db) dqa[db] = T::mfma(off.tr_operand(Ks, si, db), dsf[si], dqa[db]);
     }
-
-    if (t < t_hi) {
-      kt.store(smem + (buf ^ 1) * 2 * TILE);
-      vt.store(smem + (buf ^ 1) * 2 * TILE + TILE);
-    }
+    wait_all_loads();
     __syncthreads();
-    if (t + 2 <= t_hi) {
-      kt.load(Kp, a.k_sn, j0 + 2 * BN, a.Nk);
-      vt.load(Vp, a.v_sn, j0 + 2 * BN, a.Nk);
-    }
   }
+};
+
+template <class T, int D, int BN, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_WPE, FA_DQ_WPE))) void bwd_dq_kernel(AttnArgs a) {
+  constexpr int BM = NW * 32;
+  using Ctx = DqCtx<T, D, BN, NW>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * Ctx::TILE];
+  static_assert(2 * 2 * Ctx::TILE * 2 <= 65536, "LDS offsets must fit the 16-bit immediate");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int n_qt = (a.Nq + BM - 1) / BM;
+  const bool heavy_last = (a.causal || a.wr >= 0) && a.wl < 0;
+  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_qt, a.G, heavy_last, a.xcd_remap);
+  const int b = it.unit / a.Hkv, hk = it.unit % a.Hkv;
+  const int hq = hk * a.G + it.sub;
+  const int q0 = it.tile * BM;
+  const int qrow = q0 + wave * 32 + l32;
+
+  Ctx x;
+  x.smem = smem;
+  x.Kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  x.Vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + hk * a.v_sh;
+  x.k_sn = a.k_sn;
+  x.v_sn = a.v_sn;
+  x.Nk = a.Nk;
+  x.wave = wave;
+  x.hf = hf;
+  x.c = a.scale_log2;
+  const uint16_t* Qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh;
+  const uint16_t* dOp = static_cast<const uint16_t*>(a.dout) + b * a.o_sb + hq * a.o_sh;
+  x.lse2 = INFINITY;
+  x.dsum = 0.f;
+  if (qrow < a.Nq) {
+    const uint16_t* qr = Qp + (int64_t)qrow * a.q_sn + 8 * hf;
+    const uint16_t* dr = dOp + (int64_t)qrow * a.o_sn + 8 * hf;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      x.qf[st] = *reinterpret_cast<const u32x4*>(qr + 16 * st);
+      x.df[st] = *reinterpret_cast<const u32x4*>(dr + 16 * st);
+    }
+    const int64_t ri = ((int64_t)b * a.Hq + hq) * ((a.Nq + 127) / 128 * 128) + qrow;
+    x.lse2 = a.lse2[ri];
+    x.dsum = a.dsum[ri];
+  } else {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) x.qf[st] = x.df[st] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  x.lo_i = key_lo(a, qrow);
+  x.hi_i = key_hi(a, qrow);
+  const int q_last = min(q0 + BM, a.Nq) - 1;
+  const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
+  x.lo_max = key_lo(a, q_last);
+  x.hi_min = key_hi(a, q0);
+  const int t_lo = kv_lo / BN;
+  x.t_hi = (kv_hi >= kv_lo) ? kv_hi / BN : t_lo - 1;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) x.dqa[db] = f32x16{};
+  x.off.init(lane);
+  x.kd.init(wave, lane, a.k_sn);
+  x.vd.init(wave, lane, a.v_sn);
+
+  if (t_lo <= x.t_hi) {
+    x.kd.issue(x.Kp, a.k_sn, t_lo * BN, a.Nk, smem, wave);
+    x.vd.issue(x.Vp, a.v_sn, t_lo * BN, a.Nk, smem + Ctx::TILE, wave);
+    wait_all_loads();
+  }
+  __syncthreads();
+  int t = t_lo;
+  for (; t + 1 <= x.t_hi; t += 2) {
+    x.template step<0>(t);
+    x.template step<1>(t + 1);
+  }
+  if (t <= x.t_hi) x.template step<0>(t);
 
   if (qrow < a.Nq) {
     uint16_t* dqp = static_cast<uint16_t*>(a.dq) + b * a.q_sb + hq * a.q_sh + (int64_t)qrow * a.q_sn;
@@ -427,8 +521,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * db + 8 * g4 + 4 * hf;
         *reinterpret_cast<u32x2*>(dqp + d0) =
-            u32x2{T::pack(dqa[db][4 * g4] * sc, dqa[db][4 * g4 + 1] * sc),
-                  T::pack(dqa[db][4 * g4 + 2] * sc, dqa[db][4 * g4 + 3] * sc)};
+            u32x2{T::pack(x.dqa[db][4 * g4] * sc, x.dqa[db][4 * g4 + 1] * sc),
+                  T::pack(x.dqa[db][4 * g4 + 2] * sc, x.dqa[db][4 * g4 + 3] * sc)};
       }
     }
   }
@@ -436,26 +530,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
 
 template <class T, int D>
 static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream) {
-  constexpr int NW = 4;
-  constexpr int BMQ = 64;        // queries per dK/dV iteration
-  constexpr int BN_DQ = 64;      // keys per dQ iteration
   hipError_t e = launch_bwd_preprocess(a, stream);
   if (e != hipSuccess) return e;
   AttnArgs args = a;
   args.xcd_remap = a.xcd_remap && ((a.B * a.Hkv) % 8 == 0);
-  const int n_kt = (a.Nk + NW * 32 - 1) / (NW * 32);
+  const int n_kt = (a.Nk + FA_DKDV_NW * 32 - 1) / (FA_DKDV_NW * 32);
   const int64_t grid_kv = (int64_t)a.B * a.Hkv * n_kt;
   if (grid_kv > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, BMQ, NW>), dim3((unsigned)grid_kv), dim3(NW * 64), 0,
-                       stream, args);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, FA_DKDV_BMQ, FA_DKDV_NW>), dim3((unsigned)grid_kv),
+                       dim3(FA_DKDV_NW * 64), 0, stream, args);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int n_qt = (a.Nq + NW * 32 - 1) / (NW * 32);
+  const int n_qt = (a.Nq + FA_DQ_NW * 32 - 1) / (FA_DQ_NW * 32);
   const int64_t grid_q = (int64_t)a.B * a.Hkv * n_qt * a.G;
   if (grid_q > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, BN_DQ, NW>), dim3((unsigned)grid_q), dim3(NW * 64), 0,
-                       stream, args);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, FA_DQ_BN, FA_DQ_NW>), dim3((unsigned)grid_q), dim3(FA_DQ_NW * 64),
+                       0, stream, args);
     e = hipGetLastError();
   }
   return e;

@@ -34,7 +34,8 @@ struct AttnArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;       // (B, Hq, Nq) workspace: D_i = sum_c dout*o
+  float* dsum;       // (B, Hq, Nq_pad) workspace: D_i = sum_c dout*o (0 on padding rows)
+  float* lse2;       // (B, Hq, Nq_pad) workspace: LSE*log2(e), +inf on padding / empty rows
   int64_t q_sb, q_sn, q_sh;
   int64_t k_sb, k_sn, k_sh;
   int64_t v_sb, v_sn, v_sh;

@@ -228,9 +228,10 @@ __global__ __launch_bounds__(256) void f32_bwd_dq_kernel(AttnArgs a) {
     lo[ii] = key_lo(a, r);
     hi[ii] = key_hi(a, r);
     const int64_t ri = ((int64_t)b * a.Hq + hq) * a.Nq + r;
+    const int64_t rp = ((int64_t)b * a.Hq + hq) * ((a.Nq + 127) / 128 * 128) + r;  // padded row index
     const float L = (r < a.Nq) ? a.lse[ri] : -INFINITY;
     lse2[ii] = (L == -INFINITY) ? INFINITY : (double)L * 1.4426950408889634;
-    dsum[ii] = (r < a.Nq) ? (double)a.dsum[ri] : 0.0;
+    dsum[ii] = (r < a.Nq) ? (double)a.dsum[rp] : 0.0;
 #pragma unroll
     for (int jj = 0; jj < DP / 16; ++jj) dq[ii][jj] = 0.0;
   }
@@ -300,6 +301,7 @@ __global__ __launch_bounds__(256) void f32_bwd_dkdv_kernel(AttnArgs a) {
     const float* Qp = static_cast<const float*>(a.q) + b * a.q_sb + hq * a.q_sh;
     const float* dOp = static_cast<const float*>(a.dout) + b * a.o_sb + hq * a.o_sh;
     const int64_t rbase = ((int64_t)b * a.Hq + hq) * a.Nq;
+    const int64_t pbase = ((int64_t)b * a.Hq + hq) * ((a.Nq + 127) / 128 * 128);  // padded rows
     for (int t = t_lo; t <= t_hi; ++t) {
       const int i0 = t * kT;
       __syncthreads();
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(256) void f32_bwd_dkdv_kernel(AttnArgs a) {
         const int i = i0 + tid;
         const float L = (i < a.Nq) ? a.lse[rbase + i] : -INFINITY;
         lse2s[tid] = (L == -INFINITY) ? INFINITY : (double)L * 1.4426950408889634;
-        dsums[tid] = (i < a.Nq) ? (double)a.dsum[rbase + i] : 0.0;
+        dsums[tid] = (i < a.Nq) ? (double)a.dsum[pbase + i] : 0.0;
       }
       __syncthreads();
       // S^T[key][query] and dP^T[key][query].

@@ -70,6 +70,10 @@ fa_status check_params(const fa_params* p) {
   } else if (p->headdim != 64 && p->headdim != 128) {
     return fail(FA_ERR_UNSUPPORTED, "fp16/bf16 headdim must be 64 or 128 (got %lld)", (long long)p->headdim);
   }
+  // Kernels address a tile of up to 128 rows with 32-bit byte offsets.
+  if (p->q_strides[1] > (int64_t(1) << 22) || p->k_strides[1] > (int64_t(1) << 22) ||
+      p->v_strides[1] > (int64_t(1) << 22) || p->o_strides[1] > (int64_t(1) << 22))
+    return fail(FA_ERR_UNSUPPORTED, "sequence strides above 2^22 elements are not supported");
   const int64_t* strides[4] = {p->q_strides, p->k_strides, p->v_strides, p->o_strides};
   const char* names[4] = {"q", "k", "v", "o"};
   const int64_t eb = (int64_t)elem_bytes(p->dtype);
@@ -141,8 +145,13 @@ fa::AttnArgs make_args(const fa_params* p) {
   return a;
 }
 
+// Two float32 arrays (row sums D_i and log2-scaled LSE) of batch * nheads_q *
+// Nq_pad entries, Nq_pad = seqlen_q rounded up to a multiple of 128.
+size_t workspace_rows(const fa_params* p) {
+  return (size_t)p->batch * (size_t)p->nheads_q * (size_t)((p->seqlen_q + 127) / 128 * 128);
+}
 size_t workspace_bytes_for(const fa_params* p) {
-  const size_t n = (size_t)p->batch * (size_t)p->nheads_q * (size_t)p->seqlen_q * sizeof(float);
+  const size_t n = 2 * workspace_rows(p) * sizeof(float);
   return ((n + 255) / 256) * 256;
 }
 
@@ -215,6 +224,7 @@ fa_status fa_bwd(const fa_params* params, const void* dout, const void* q, const
   a.q = q; a.k = k; a.v = v; a.o = const_cast<void*>(o); a.lse = const_cast<float*>(lse);
   a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
   a.dsum = static_cast<float*>(workspace);
+  a.lse2 = a.dsum + workspace_rows(params);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const hipError_t e = (params->dtype == FA_F32) ? fa::launch_bwd_f32(a, st) : fa::launch_bwd_mfma(a, st);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));

@@ -197,3 +197,76 @@ __device__ __forceinline__ u32x4 swz_tr_operand(const uint16_t* tile, int s, int
 }
 
 }  // namespace fa
+
+namespace fa {
+
+// ===========================================================================
+// Direct global -> LDS tile loads (global_load_lds_dwordx4).
+//
+// One instruction moves 16 bytes per lane into LDS at (wave-uniform base) +
+// 16 * lane, i.e. 1 KB of consecutive LDS per wave.  The swizzled layout above
+// is produced by choosing each lane's global address: LDS chunk slot `lane` of
+// 1 KB block j is row j*RPB + lane / CPR, physical chunk lane % CPR, which
+// holds logical chunk (lane % CPR) ^ sw(row).  Each lane's byte offsets
+// (relative to the tile's first row) are computed once per kernel; a tile
+// load then adds one wave-uniform base pointer.
+// ===========================================================================
+// 16 bytes per lane from global memory straight into LDS at
+// lds_block + 16 * lane (lds_block must be the same for the whole wave).
+__device__ __forceinline__ void dma16(const void* g, uint16_t* lds_block) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_block, 16, 0, 0);
+}
+
+template <int D, int ROWS, int NW>
+struct DmaTile {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int RPB = 64 / CPR;              // rows per 1 KB block
+  static constexpr int NBLK = ROWS / RPB;           // 1 KB blocks per tile
+  static constexpr int PER_WAVE = (NBLK + NW - 1) / NW;
+  static_assert(ROWS % RPB == 0, "tile rows must fill whole 1 KB blocks");
+  uint32_t off[PER_WAVE];  // byte offsets of this lane's chunk in each of its blocks
+  int lane_row, lane_pc;
+
+  __device__ __forceinline__ void init(int wave, int lane, int64_t row_stride_elems) {
+    lane_row = lane / CPR;
+    lane_pc = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int j = wave + i * NW;
+      const int r = j * RPB + lane_row;
+      const int c = lane_pc ^ Swz<D>::sw(r);
+      off[i] = (uint32_t)(r * row_stride_elems * 2 + c * 16);
+    }
+  }
+  // Rows row0 .. row0+ROWS-1 of a tensor whose rows start every row_stride
+  // elements.  Rows at or beyond nrows (>= 1) re-read row nrows-1 (those keys
+  // are masked; a finite copy keeps 0 * value finite).
+  __device__ __forceinline__ void issue(const uint16_t* base, int64_t row_stride, int row0, int nrows,
+                                        uint16_t* lds_tile, int wave) const {
+    const char* tb = reinterpret_cast<const char*>(base + (int64_t)row0 * row_stride);
+    if (row0 + ROWS <= nrows) {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int j = wave + i * NW;
+        if (NBLK % NW == 0 || j < NBLK) dma16(tb + off[i], lds_tile + j * 512);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int j = wave + i * NW;
+        if (NBLK % NW == 0 || j < NBLK) {
+          const int r = j * RPB + lane_row;
+          const int row = min(row0 + r, nrows - 1);
+          const int c = lane_pc ^ Swz<D>::sw(r);
+          dma16(reinterpret_cast<const char*>(base + (int64_t)row * row_stride) + c * 16, lds_tile + j * 512);
+        }
+      }
+    }
+  }
+};
+
+// Wait until this wave's direct-to-LDS loads (and every other outstanding
+// memory operation of the wave) have completed.
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
+}  // namespace fa

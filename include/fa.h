@@ -105,9 +105,10 @@ fa_status fa_fwd(const fa_params* params, const void* q, const void* k, const vo
                  void* o, float* lse, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these parameters (a float32
- * per-row array D_i = sum_c dout[i,c] * o[i,c], batch * nheads_q * seqlen_q
- * entries, rounded up to 256 bytes).  Writes the size to *bytes.
+ * Bytes of device workspace fa_bwd needs for these parameters: two float32
+ * per-row arrays (D_i = sum_c dout[i,c] * o[i,c], and the LSE in base 2) of
+ * batch * nheads_q * Nq_pad entries each, Nq_pad = seqlen_q rounded up to a
+ * multiple of 128; the total is rounded up to 256 bytes.  Writes it to *bytes.
  */
 fa_status fa_bwd_workspace_size(const fa_params* params, size_t* bytes);
 

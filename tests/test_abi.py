@@ -164,7 +164,8 @@ def test_workspace_size_and_check(lib):
     p = params()
     n = ctypes.c_size_t()
     assert lib.fa_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == N.FA_OK
-    assert n.value == ((4 * 2 * 4 * 64 + 255) // 256) * 256
+    # two float32 arrays of batch * nheads_q * (seqlen_q rounded up to 128)
+    assert n.value == ((2 * 4 * 2 * 4 * 128 + 255) // 256) * 256
     assert lib.fa_bwd_workspace_size(ctypes.byref(p), None) == N.FA_ERR_INVALID_ARG
     assert call_bwd(lib, p, ws_bytes=n.value - 4) == N.FA_ERR_INVALID_ARG
     assert b"workspace" in lib.fa_last_error()
@@ -219,3 +220,10 @@ def test_missing_library_fails_loudly(tmp_path):
             "try:\n    N.load_library()\nexcept RuntimeError as e:\n    print('RAISED', 'missing' in str(e))\n")
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert "RAISED True" in out.stdout, out.stderr
+
+
+def test_library_has_no_undefined_kernel_symbols(lib):
+    # Every kernel launcher's host stub must be defined in the library itself.
+    out = subprocess.run(["nm", "-D", "--undefined-only", N.LIB_PATH], capture_output=True, text=True).stdout
+    missing = [l for l in out.splitlines() if "_ZN2fa" in l]
+    assert not missing, missing
