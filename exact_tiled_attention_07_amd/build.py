@@ -41,9 +41,14 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def _compile(src, build_dir=BUILD_DIR, defines=()):
+# Per-source extra compiler flags.
+SOURCE_FLAGS = {}
+
+
+def _compile(src, build_dir=BUILD_DIR, defines=(), extra=None):
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, *[f"-D{d}" for d in defines], "-x", "hip", "-c",
+    flags = list(SOURCE_FLAGS.get(src, ())) + list((extra or {}).get(src, ()))
+    cmd = [hipcc(), *COMMON_FLAGS, *flags, *[f"-D{d}" for d in defines], "-x", "hip", "-c",
            os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -53,12 +58,13 @@ def _compile(src, build_dir=BUILD_DIR, defines=()):
     return obj, err
 
 
-def build(verbose=True, lib_path=LIB_PATH, build_dir=BUILD_DIR, defines=()):
+def build(verbose=True, lib_path=LIB_PATH, build_dir=BUILD_DIR, defines=(), extra_flags=None):
     """Compile every source and link libfa.so; returns the library path.
-    ``defines`` (NAME=VALUE strings) override the kernels' launch configuration."""
+    ``defines`` (NAME=VALUE strings) override the kernels' launch configuration;
+    ``extra_flags`` maps a source file name to additional compiler flags."""
     os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        results = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+        results = list(ex.map(lambda src: _compile(src, build_dir, defines, extra_flags), SOURCES))
     for _, err in results:
         if err.strip() and verbose:
             print(err, file=sys.stderr)

@@ -205,7 +205,34 @@ struct DkdvCtx {
     const float* dsums = lse2s + BMQ;
     const int i0 = (qt_lo + w % n_qt) * BMQ;
     if (w + 1 < n_items) issue<1 - BUF>(w + 1);
+    const int i_end = min(i0 + BMQ, a->Nq) - 1;
+    const bool full = (key_lo(*a, i_end) <= k0) && (key_hi(*a, i0) >= k_last);
+    step_items(Qs, dOs, lse2s, dsums, i0, full);
+    wait_all_loads();
+    __syncthreads();
+  }
 
+  // P = exp2(s*c - lse2), dS = P * (dP - D) for one 32-query block, packed as
+  // B operands pf[2], dsf[2] (entries r of block qb are query 32*qb + 8*(r/4)
+  // + 4*hf + r%4; l4/d4 hold the row statistics of that order).
+  __device__ __forceinline__ void softmax_grad_elem(const f32x16& sv, const f32x16& dpv, const f32x4 (&l4)[4],
+                                                    const f32x4 (&d4)[4], int r, float (&pb)[8], float (&db_)[8],
+                                                    u32x4* pf, u32x4* dsf) {
+    const float pr = fast_exp2(fmaf(sv[r], c, -l4[r >> 2][r & 3]));
+    pb[r & 7] = pr;
+    db_[r & 7] = pr * (dpv[r] - d4[r >> 2][r & 3]);
+    if ((r & 7) == 7) {
+      pf[r >> 3] = u32x4{T::pack(pb[0], pb[1]), T::pack(pb[2], pb[3]), T::pack(pb[4], pb[5]), T::pack(pb[6], pb[7])};
+      dsf[r >> 3] = u32x4{T::pack(db_[0], db_[1]), T::pack(db_[2], db_[3]), T::pack(db_[4], db_[5]),
+                          T::pack(db_[6], db_[7])};
+    }
+  }
+
+  // The products of one item.  (A hand-pipelined variant that overlaps the
+  // VALU work of one 32-query block with the MFMAs of the other needs more
+  // than the 512 registers a wave can hold here and was slower.)
+  __device__ __forceinline__ void step_items(const char* Qs, const char* dOs, const float* lse2s, const float* dsums,
+                                             int i0, bool full) {
     // S = Q K^T and dP = dO V^T; [qb][r] is query i0 + 32*qb + 8*(r/4) + 4*hf + r%4.
     f32x16 s[BMQ / 32], dp[BMQ / 32];
 #pragma unroll
@@ -218,9 +245,6 @@ struct DkdvCtx {
         dp[qb] = T::mfma(off.row_chunk(dOs, qb, st), vf[st], dp[qb]);
       }
     }
-    // Mask: exact per-element test only where the tile pair is not fully visible.
-    const int i_end = min(i0 + BMQ, a->Nq) - 1;
-    const bool full = (key_lo(*a, i_end) <= k0) && (key_hi(*a, i0) >= k_last);
     if (!full) {
 #pragma unroll
       for (int qb = 0; qb < BMQ / 32; ++qb) {
@@ -231,31 +255,18 @@ struct DkdvCtx {
         }
       }
     }
-    // P = exp2(s*c - lse2) and dS = P * (dP - D), both as B operands.
     u32x4 pf[BMQ / 16], dsf[BMQ / 16];
 #pragma unroll
     for (int qb = 0; qb < BMQ / 32; ++qb) {
-      float p[16], ds[16];
+      f32x4 l4[4], d4[4];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + 32 * qb + 8 * g4 + 4 * hf);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsums + 32 * qb + 8 * g4 + 4 * hf);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          p[r] = fast_exp2(fmaf(s[qb][r], c, -l4[e]));
-          ds[r] = p[r] * (dp[qb][r] - d4[e]);
-        }
+        l4[g4] = *reinterpret_cast<const f32x4*>(lse2s + 32 * qb + 8 * g4 + 4 * hf);
+        d4[g4] = *reinterpret_cast<const f32x4*>(dsums + 32 * qb + 8 * g4 + 4 * hf);
       }
+      float pb[8], dbf[8];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const float* pp = &p[8 * tt];
-        const float* qq = &ds[8 * tt];
-        pf[2 * qb + tt] = u32x4{T::pack(pp[0], pp[1]), T::pack(pp[2], pp[3]), T::pack(pp[4], pp[5]),
-                                T::pack(pp[6], pp[7])};
-        dsf[2 * qb + tt] = u32x4{T::pack(qq[0], qq[1]), T::pack(qq[2], qq[3]), T::pack(qq[4], qq[5]),
-                                 T::pack(qq[6], qq[7])};
-      }
+      for (int r = 0; r < 16; ++r) softmax_grad_elem(s[qb], dp[qb], l4, d4, r, pb, dbf, pf + 2 * qb, dsf + 2 * qb);
     }
     // dV^T += dO^T P and dK^T += Q^T dS, operands read transposed from the tiles.
 #pragma unroll
@@ -266,8 +277,6 @@ struct DkdvCtx {
         dka[db] = T::mfma(off.tr_operand(Qs, si, db), dsf[si], dka[db]);
       }
     }
-    wait_all_loads();
-    __syncthreads();
   }
 };
 
