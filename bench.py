@@ -75,6 +75,59 @@ def flops(w):
     return fwd, 2.5 * fwd
 
 
+# HBM bytes per launch of the dK/dV kernel on the bench workload, from two
+# rocprofv3 --pmc runs of "python3 bench.py --steps 2 --warmup 1
+# --no-cpu-baseline" (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
+# scaled by the factor that the same counter needs to read 512 MiB for the
+# plain copy of "python3 bench.py --copy-probe".  They describe the kernel
+# built from the sources whose SHA-256 is recorded here and are reported as
+# null for any other source.
+DKDV_TRAFFIC = None
+
+
+def kernel_sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("bwd_mfma.hip", "common.hpp", "tile_io.hpp"):
+        with open(os.path.join(ROOT, "exact_tiled_attention_07_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def kernel_table(w, f_fwd, f_bwd, ms):
+    """Per-kernel figures for one step.  Algorithmic FLOP per launch: the
+    forward kernel does both forward products; the backward's five products
+    per visible pair (S = QK^T again, dP = dO V^T, dV = P^T dO, dK = dS^T Q,
+    dQ = dS K) split 4 to the dK/dV kernel and 1 to the dQ kernel (which also
+    recomputes S and dP: work that is not counted).  The preprocess kernel is
+    rated against HBM: it reads dO and O and the LSE and writes two float32
+    rows statistics per query row (padded to 128 rows)."""
+    e = 2
+    rows = w.batch * w.nheads_q * w.seqlen
+    rows_pad = w.batch * w.nheads_q * (-(-w.seqlen // 128) * 128)
+    prep_bytes = 2 * rows * w.headdim * e + 4 * rows + 2 * 4 * rows_pad
+    spec = [
+        ("fwd_mfma_kernel<BF16,128,64,8> (fa_fwd)", "mfma", f_fwd),
+        ("bwd_preprocess_kernel<2> (fa_bwd_stage PREPARE)", "hbm", prep_bytes),
+        ("bwd_dkdv_kernel<BF16,128,64,4> (fa_bwd_stage DKDV)", "mfma", 0.8 * f_bwd),
+        ("bwd_dq_kernel<BF16,128,64,8> (fa_bwd_stage DQ)", "mfma", 0.2 * f_bwd),
+    ]
+    out = []
+    for (name, bound, work), t in zip(spec, ms):
+        if bound == "mfma":
+            ach, peak, unit = work / (t * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = work / (t * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+        row = {"kernel": name, "ms": round(t, 4), "bound": bound, "achieved": round(ach, 2), "peak": peak,
+               "unit": unit, "frac": round(ach / peak, 4)}
+        if "dkdv" in name:
+            row["traffic"] = None
+            if DKDV_TRAFFIC and DKDV_TRAFFIC["sources_sha256"] == kernel_sources_sha():
+                row["traffic"] = DKDV_TRAFFIC["bytes_per_launch"]
+        out.append(row)
+    return out
+
+
 def cpu_baseline(w, q, k, v, do, budget_s):
     """Time the float64 oracle on whole heads of the workload until budget_s is
     reached (at least one head, at most one kv group); report TFLOP/s."""
@@ -154,39 +207,53 @@ def main():
     ws = torch.empty(fa.bwd_workspace_size(params), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    stages = (fa.FA_BWD_PREPARE, fa.FA_BWD_DKDV, fa.FA_BWD_DQ)
+
     def step(ev=None):
+        # fa_fwd, then fa_bwd as its three stages (bitwise the same as one
+        # fa_bwd call), with an event between launches so that every kernel is
+        # timed on the stream it runs on.
         if ev is not None:
             ev[0].record(stream)
         fa.fwd(q, k, v, out=o, lse=lse, **kw)
+        for i, st in enumerate(stages):
+            if ev is not None:
+                ev[1 + i].record(stream)
+            fa.bwd(do, q, k, v, o, lse, dq=dq, dk=dk, dv=dv, workspace=ws, stage=st, **kw)
         if ev is not None:
-            ev[1].record(stream)
-        fa.bwd(do, q, k, v, o, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
-        if ev is not None:
-            ev[2].record(stream)
+            ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in events]
-    step_ms = [e[0].elapsed_time(e[2]) for e in events]
     assert torch.isfinite(o).all() and torch.isfinite(dq).all()
+
+    def avg_ms(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in events) / len(events)
 
     f_fwd, f_bwd = flops(w)
     ms_per_step = wall * 1e3 / args.steps
     value = (f_fwd + f_bwd) * args.steps / wall / 1e12
-    fwd_avg = sum(fwd_ms) / len(fwd_ms)
-    bwd_avg = sum(bwd_ms) / len(bwd_ms)
-    fwd_tflops = f_fwd / (fwd_avg * 1e-3) / 1e12
-    bwd_tflops = f_bwd / (bwd_avg * 1e-3) / 1e12
+    fwd_avg, bwd_avg, step_avg = avg_ms(0, 1), avg_ms(1, 4), avg_ms(0, 4)
+    kernels = kernel_table(w, f_fwd, f_bwd, [avg_ms(i, i + 1) for i in range(4)])
+    dom = max(kernels, key=lambda r: r["ms"])
+    roof = {
+        "kernel": dom["kernel"],
+        "bound": dom["bound"],
+        "achieved": dom["achieved"],
+        "peak": dom["peak"],
+        "unit": dom["unit"],
+        "frac": dom["frac"],
+        "traffic": dom.get("traffic"),
+    }
 
     out = {
         "metric": METRIC,
@@ -209,18 +276,11 @@ def main():
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(fwd_avg, 4),
         "bwd_ms": round(bwd_avg, 4),
-        "fwd_tflops": round(fwd_tflops, 2),
-        "bwd_tflops": round(bwd_tflops, 2),
-        "event_ms_per_step": round(sum(step_ms) / len(step_ms), 4),
-        "roofline": {
-            "kernel": "fwd_mfma_kernel (fa_fwd, one launch per call)",
-            "bound": "mfma",
-            "achieved": round(fwd_tflops, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
-        },
+        "fwd_tflops": round(f_fwd / (fwd_avg * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / (bwd_avg * 1e-3) / 1e12, 2),
+        "event_ms_per_step": round(step_avg, 4),
+        "roofline": roof,
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q_c, k_c, v_c, do_c, args.cpu_seconds)

@@ -11,7 +11,8 @@ Python binding: torch provides device memory and streams only.
 """
 
 from ._native import (  # noqa: F401
-    FA_BF16, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_F16, FA_F32, FA_OK, SIGNATURES,
+    FA_BF16, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_PREPARE, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED,
+    FA_F16, FA_F32, FA_OK, SIGNATURES,
     FaError, FaParams, attention, bwd, bwd_workspace_size, fwd, library_path, load_library,
     make_params, version,
 )

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_BWD_PREPARE, FA_BWD_DKDV, FA_BWD_DQ = 0, 1, 2
 _TORCH_DTYPE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
 
 # Every function the header declares, with its ctypes signature.
@@ -49,6 +50,8 @@ SIGNATURES = {
     "fa_fwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
     "fa_bwd_workspace_size": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
     "fa_bwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "fa_bwd_stage": (ctypes.c_int, [_P, ctypes.c_int, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t,
+                                    _V]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_version": (ctypes.c_int, []),
@@ -176,11 +179,16 @@ def bwd_workspace_size(params):
 
 
 def bwd(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1), scale=None,
-        dq=None, dk=None, dv=None, workspace=None):
+        dq=None, dk=None, dv=None, workspace=None, stage=None):
     """Exact attention backward: returns (dq, dk, dv) of L = sum(out * dout).
 
     dout uses out's layout; dq gets q's strides, dk/dv get k's and v's.
+    With ``stage`` (FA_BWD_PREPARE, FA_BWD_DKDV or FA_BWD_DQ) only that stage
+    of the backward pass runs (fa_bwd_stage); the caller then passes the same
+    ``workspace`` to all three stages.
     """
+    if stage is not None and workspace is None:
+        raise ValueError("a single backward stage needs the caller's workspace")
     _require_gpu(dout, q, k, v, out, lse)
     lib = load_library()
     if dout.shape != q.shape or dout.dtype != q.dtype or dout.stride() != out.stride():
@@ -198,10 +206,13 @@ def bwd(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1), scale=No
     need = bwd_workspace_size(p)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ptrs = (_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(workspace), workspace.numel(), _stream(q.device))
     with torch.cuda.device(q.device):
-        _check(lib.fa_bwd(ctypes.byref(p), _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
-                          _stream(q.device)))
+        if stage is None:
+            _check(lib.fa_bwd(ctypes.byref(p), *ptrs))
+        else:
+            _check(lib.fa_bwd_stage(ctypes.byref(p), int(stage), *ptrs))
     return dq, dk, dv
 
 

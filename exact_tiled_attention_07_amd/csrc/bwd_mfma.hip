@@ -177,11 +177,18 @@ struct DkdvCtx {
   SwzOffsets<D> off;
   DmaTile<D, BMQ, NW> qd, dd;
 
-  // Start the loads of work item w (query head of the group, query tile).
+  // Work item w -> (query head of the group, first query row).  Query tiles
+  // run from the last one down, with the heads of the group innermost: the
+  // workgroups of one K/V head that run at the same time then read the same
+  // Q/dO tiles at about the same time, and those come from L2.
+  __device__ __forceinline__ int item_row(int w) const { return (qt_lo + n_qt - 1 - w / a->G) * BMQ; }
+  __device__ __forceinline__ int item_head(int w) const { return hk * a->G + w % a->G; }
+
+  // Start the loads of work item w.
   template <int BUF>
   __device__ __forceinline__ void issue(int w) {
-    const int g = w / n_qt, i0 = (qt_lo + w % n_qt) * BMQ;
-    const int hq = hk * a->G + g;
+    const int i0 = item_row(w);
+    const int hq = item_head(w);
     qd.issue(static_cast<const uint16_t*>(a->q) + b * a->q_sb + hq * a->q_sh, a->q_sn, i0, a->Nq,
              smem + BUF * 2 * TILE, wave);
     dd.issue(static_cast<const uint16_t*>(a->dout) + b * a->o_sb + hq * a->o_sh, a->o_sn, i0, a->Nq,
@@ -203,7 +210,7 @@ struct DkdvCtx {
     const char* dOs = Qs + TILE * 2;
     const float* lse2s = rstat + BUF * 2 * BMQ;
     const float* dsums = lse2s + BMQ;
-    const int i0 = (qt_lo + w % n_qt) * BMQ;
+    const int i0 = item_row(w);
     if (w + 1 < n_items) issue<1 - BUF>(w + 1);
     const int i_end = min(i0 + BMQ, a->Nq) - 1;
     const bool full = (key_lo(*a, i_end) <= k0) && (key_hi(*a, i0) >= k_last);
@@ -538,14 +545,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
 }
 
 template <class T, int D>
-static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream) {
-  hipError_t e = launch_bwd_preprocess(a, stream);
-  if (e != hipSuccess) return e;
+static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream, int stages) {
+  hipError_t e = hipSuccess;
+  if (stages & kStagePrepare) {
+    e = launch_bwd_preprocess(a, stream);
+    if (e != hipSuccess) return e;
+  }
   AttnArgs args = a;
   args.xcd_remap = a.xcd_remap && ((a.B * a.Hkv) % 8 == 0);
   const int n_kt = (a.Nk + FA_DKDV_NW * 32 - 1) / (FA_DKDV_NW * 32);
   const int64_t grid_kv = (int64_t)a.B * a.Hkv * n_kt;
-  if (grid_kv > 0) {
+  if (grid_kv > 0 && (stages & kStageDkdv)) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, FA_DKDV_BMQ, FA_DKDV_NW>), dim3((unsigned)grid_kv),
                        dim3(FA_DKDV_NW * 64), 0, stream, args);
     e = hipGetLastError();
@@ -553,7 +563,7 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream) {
   }
   const int n_qt = (a.Nq + FA_DQ_NW * 32 - 1) / (FA_DQ_NW * 32);
   const int64_t grid_q = (int64_t)a.B * a.Hkv * n_qt * a.G;
-  if (grid_q > 0) {
+  if (grid_q > 0 && (stages & kStageDq)) {
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, FA_DQ_BN, FA_DQ_NW>), dim3((unsigned)grid_q), dim3(FA_DQ_NW * 64),
                        0, stream, args);
     e = hipGetLastError();
@@ -561,13 +571,13 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream) {
   return e;
 }
 
-hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t stream, int stages) {
   if (a.dtype == kBF16) {
-    if (a.D == 128) return launch_bwd_t<BF16, 128>(a, stream);
-    if (a.D == 64) return launch_bwd_t<BF16, 64>(a, stream);
+    if (a.D == 128) return launch_bwd_t<BF16, 128>(a, stream, stages);
+    if (a.D == 64) return launch_bwd_t<BF16, 64>(a, stream, stages);
   } else if (a.dtype == kF16) {
-    if (a.D == 128) return launch_bwd_t<F16, 128>(a, stream);
-    if (a.D == 64) return launch_bwd_t<F16, 64>(a, stream);
+    if (a.D == 128) return launch_bwd_t<F16, 128>(a, stream, stages);
+    if (a.D == 64) return launch_bwd_t<F16, 64>(a, stream, stages);
   }
   return hipErrorInvalidValue;
 }

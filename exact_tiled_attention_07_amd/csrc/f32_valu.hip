@@ -363,11 +363,14 @@ hipError_t launch_fwd_f32(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_f32(const AttnArgs& a, hipStream_t stream) {
-  hipError_t e = launch_bwd_preprocess(a, stream);
-  if (e != hipSuccess) return e;
+hipError_t launch_bwd_f32(const AttnArgs& a, hipStream_t stream, int stages) {
+  hipError_t e = hipSuccess;
+  if (stages & kStagePrepare) {
+    e = launch_bwd_preprocess(a, stream);
+    if (e != hipSuccess) return e;
+  }
   const int64_t grid_kv = (int64_t)a.B * a.Hkv * ((a.Nk + kT - 1) / kT);
-  if (grid_kv > 0) {
+  if (grid_kv > 0 && (stages & kStageDkdv)) {
     if (a.D <= 64)
       hipLaunchKernelGGL(f32_bwd_dkdv_kernel<64>, dim3((unsigned)grid_kv), dim3(256), 0, stream, a);
     else
@@ -376,7 +379,7 @@ hipError_t launch_bwd_f32(const AttnArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const int64_t grid_q = (int64_t)a.B * a.Hq * ((a.Nq + kT - 1) / kT);
-  if (grid_q > 0) {
+  if (grid_q > 0 && (stages & kStageDq)) {
     if (a.D <= 64)
       hipLaunchKernelGGL(f32_bwd_dq_kernel<64>, dim3((unsigned)grid_q), dim3(256), 0, stream, a);
     else

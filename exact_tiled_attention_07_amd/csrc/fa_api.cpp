@@ -189,9 +189,13 @@ fa_status fa_bwd_workspace_size(const fa_params* params, size_t* bytes) {
   return FA_OK;
 }
 
-fa_status fa_bwd(const fa_params* params, const void* dout, const void* q, const void* k, const void* v,
-                 const void* o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status run_bwd(const fa_params* params, int stages, const void* dout, const void* q, const void* k,
+                  const void* v, const void* o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   fa_status s = check_params(params);
   if (s != FA_OK) return s;
   const bool q_nonempty = !empty_problem(params);
@@ -226,9 +230,33 @@ fa_status fa_bwd(const fa_params* params, const void* dout, const void* q, const
   a.dsum = static_cast<float*>(workspace);
   a.lse2 = a.dsum + workspace_rows(params);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = (params->dtype == FA_F32) ? fa::launch_bwd_f32(a, st) : fa::launch_bwd_mfma(a, st);
+  const hipError_t e =
+      (params->dtype == FA_F32) ? fa::launch_bwd_f32(a, st, stages) : fa::launch_bwd_mfma(a, st, stages);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd(const fa_params* params, const void* dout, const void* q, const void* k, const void* v,
+                 const void* o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return run_bwd(params, fa::kStageAll, dout, q, k, v, o, lse, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_stage(const fa_params* params, int stage, const void* dout, const void* q, const void* k,
+                       const void* v, const void* o, const float* lse, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int mask = 0;
+  switch (stage) {
+    case FA_BWD_PREPARE: mask = fa::kStagePrepare; break;
+    case FA_BWD_DKDV: mask = fa::kStageDkdv; break;
+    case FA_BWD_DQ: mask = fa::kStageDq; break;
+    default: return fail(FA_ERR_INVALID_ARG, "unknown backward stage %d", stage);
+  }
+  return run_bwd(params, mask, dout, q, k, v, o, lse, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_string(fa_status status) {

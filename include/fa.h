@@ -70,6 +70,13 @@ typedef enum {
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 
+/* The three stages of fa_bwd (see fa_bwd_stage). */
+typedef enum {
+  FA_BWD_PREPARE = 0, /* per-row statistics of the backward pass -> workspace */
+  FA_BWD_DKDV = 1,    /* dk and dv, reading the workspace */
+  FA_BWD_DQ = 2       /* dq, reading the workspace */
+} fa_bwd_stage_id;
+
 typedef struct {
   int64_t batch;
   int64_t seqlen_q, seqlen_k;
@@ -133,6 +140,28 @@ fa_status fa_bwd_workspace_size(const fa_params* params, size_t* bytes);
 fa_status fa_bwd(const fa_params* params, const void* dout, const void* q, const void* k,
                  const void* v, const void* o, const float* lse, void* dq, void* dk, void* dv,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One stage of fa_bwd, with the same arguments and the same validation.
+ * fa_bwd is exactly FA_BWD_PREPARE, FA_BWD_DKDV, FA_BWD_DQ on one stream;
+ * the stages are exposed so that a caller can time them or order them
+ * itself ([P4] section "长序列注意力为什么会爆内存" for the recomputation
+ * each stage performs):
+ *   FA_BWD_PREPARE  writes D_i = sum_c dout_ic o_ic and the forward LSE
+ *                   (rescaled to base 2) of every query row into workspace;
+ *                   reads dout, o, lse.  dq, dk, dv are not touched.
+ *   FA_BWD_DKDV     writes dk and dv (fully overwritten); reads q, k, v,
+ *                   dout and the workspace.
+ *   FA_BWD_DQ       writes dq (fully overwritten); reads q, k, v, dout and
+ *                   the workspace (and lse for fp32).
+ * DKDV and DQ must run after PREPARE of the same params, inputs and
+ * workspace has completed (stream order, or an event); they do not depend
+ * on each other.  Every pointer argument is required exactly as for fa_bwd,
+ * whichever stage runs.  An unknown stage is FA_ERR_INVALID_ARG.
+ */
+fa_status fa_bwd_stage(const fa_params* params, int stage, const void* dout, const void* q,
+                       const void* k, const void* v, const void* o, const float* lse, void* dq,
+                       void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static string naming a status code. */
 const char* fa_status_string(fa_status status);

@@ -34,7 +34,8 @@ def header_functions():
 
 def test_header_declares_expected_entry_points():
     assert header_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error", "fa_version"])
+        ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error",
+         "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -109,6 +110,13 @@ def call_bwd(lib, p, ws=W, ws_bytes=1 << 30, dq=0x70000, dk=0x80000, dv=0x90000)
     return lib.fa_bwd(ctypes.byref(p), 0xA0000, A, B_, C, O, L, dq, dk, dv, ws, ws_bytes, None)
 
 
+def call_stage(lib, p, stage, ws=W, ws_bytes=1 << 30, dq=0x70000, dk=0x80000, dv=0x90000):
+    return lib.fa_bwd_stage(ctypes.byref(p), stage, 0xA0000, A, B_, C, O, L, dq, dk, dv, ws, ws_bytes, None)
+
+
+STAGES = (N.FA_BWD_PREPARE, N.FA_BWD_DKDV, N.FA_BWD_DQ)
+
+
 INVALID = [
     ("nheads not divisible", dict(nheads_q=6, nheads_kv=4)),
     ("negative batch", dict(batch=-1)),
@@ -141,12 +149,35 @@ def test_invalid_arguments(lib, name, kw):
     assert call_fwd(lib, params(**kw)) == N.FA_ERR_INVALID_ARG
     assert lib.fa_last_error() != b""
     assert call_bwd(lib, params(**kw)) == N.FA_ERR_INVALID_ARG
+    for st in STAGES:
+        assert call_stage(lib, params(**kw), st) == N.FA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("name,kw", UNSUPPORTED, ids=[x[0] for x in UNSUPPORTED])
 def test_unsupported_arguments(lib, name, kw):
     assert call_fwd(lib, params(**kw)) == N.FA_ERR_UNSUPPORTED
     assert call_bwd(lib, params(**kw)) == N.FA_ERR_UNSUPPORTED
+    for st in STAGES:
+        assert call_stage(lib, params(**kw), st) == N.FA_ERR_UNSUPPORTED
+
+
+def test_backward_stage_validation(lib):
+    # Unknown stages are rejected; every stage checks every pointer and the
+    # workspace exactly as fa_bwd does.
+    for bad in (-1, 3, 1 << 20):
+        assert call_stage(lib, params(), bad) == N.FA_ERR_INVALID_ARG
+        assert b"stage" in lib.fa_last_error()
+    p = params()
+    n = ctypes.c_size_t()
+    assert lib.fa_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == N.FA_OK
+    for st in STAGES:
+        assert call_stage(lib, p, st, dq=None) == N.FA_ERR_INVALID_ARG
+        assert call_stage(lib, p, st, dk=A) == N.FA_ERR_INVALID_ARG
+        assert call_stage(lib, p, st, ws_bytes=n.value - 4) == N.FA_ERR_INVALID_ARG
+        assert b"workspace" in lib.fa_last_error()
+        pe = params(batch=0)
+        assert lib.fa_bwd_stage(ctypes.byref(pe), st, None, None, None, None, None, None, None, None, None,
+                                None, 0, None) == N.FA_OK
 
 
 def test_null_and_misaligned_pointers(lib):
@@ -206,6 +237,8 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
     # cleanly (no kernel is ever launched without a device).
     assert call_fwd(lib, params()) == N.FA_ERR_HIP
     assert b"hip" in lib.fa_last_error().lower()
+    for st in STAGES:
+        assert call_stage(lib, params(), st) == N.FA_ERR_HIP
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -175,6 +175,23 @@ def test_bitwise_repeatable(dtype):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_backward_stages_equal_fa_bwd(dtype):
+    # fa_bwd_stage PREPARE then DQ then DKDV (the two gradient stages in the
+    # opposite order to fa_bwd's) gives fa_bwd's gradients bit for bit.
+    q, k, v, do = (t.cuda() for t in random_qkv((2, 333, 8, 64), (2, 333, 4, 64), dtype, seed=17))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    ref = fa.bwd(do, q, k, v, o, lse, causal=True)
+    p = fa.make_params(q, k, v, o, causal=True)
+    ws = torch.empty(fa.bwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.full_like(q, 7.0), torch.full_like(k, 7.0), torch.full_like(v, 7.0)
+    for st in (fa.FA_BWD_PREPARE, fa.FA_BWD_DQ, fa.FA_BWD_DKDV):
+        fa.bwd(do, q, k, v, o, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws, stage=st)
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv), ref):
+        assert torch.equal(a, b)
+
+
 def test_strided_packed_qkv_matches_contiguous():
     qkv = torch.randn(2, 200, 3, 8, 128, generator=torch.Generator().manual_seed(15)).to(torch.bfloat16).cuda()
     q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
