@@ -21,8 +21,9 @@
 // exp2(s*c - m*c) with c = scale*log2(e), one FMA and one v_exp_f32.
 // K and V tiles sit in LDS row-major with a chunk swizzle (tile_io.hpp); V^T
 // operands come straight from the row-major tile through the transposing LDS
-// read.  The loop is software-pipelined: the MFMAs of S(t+1) are issued next to
-// the softmax VALU work of tile t, then O += V(t)^T P(t)^T.
+// read.  Tiles are double buffered: each step first issues the direct-to-LDS
+// loads of tile t+1 into the other buffer, then computes tile t; one barrier
+// per tile.
 #include <type_traits>
 
 #include "common.hpp"
