@@ -112,7 +112,7 @@ def kernel_table(w, f_fwd, f_bwd, ms):
     spec = [
         ("fwd_mfma_kernel<BF16,128,64,8> (fa_fwd)", "mfma", f_fwd),
         ("bwd_preprocess_kernel<2> (fa_bwd_stage PREPARE)", "hbm", prep_bytes),
-        ("bwd_dkdv_kernel<BF16,128,64,4> (fa_bwd_stage DKDV)", "mfma", 0.8 * f_bwd),
+        ("bwd_dkdv_ws_kernel<BF16,128,64> (fa_bwd_stage DKDV)", "mfma", 0.8 * f_bwd),
         ("bwd_dq_kernel<BF16,128,64,8> (fa_bwd_stage DQ)", "mfma", 0.2 * f_bwd),
     ]
     out = []

@@ -116,6 +116,9 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
 #ifndef FA_DKDV_WPE
 #define FA_DKDV_WPE 1
 #endif
+#ifndef FA_DKDV_WS
+#define FA_DKDV_WS 1  // dK/dV with specialised score and gradient waves
+#endif
 #ifndef FA_DQ_BN
 #define FA_DQ_BN 64  // keys per dQ iteration
 #endif
@@ -378,6 +381,366 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DKDV
 }
 
 // ---------------------------------------------------------------------------
+// dK / dV with specialised waves.
+//
+// One workgroup per (batch, kv head, tile of 32*KW keys) runs 2*KW waves:
+//   score waves    (0 .. KW-1)   hold the K and V rows of their 32 keys as MFMA
+//                  B operands; per item they compute S = Q K^T and dP = dO V^T,
+//                  then P = exp2(s*c - lse2) and dS = P * (dP - D), and write P
+//                  and dS to LDS exactly as the B-operand registers they are
+//                  (16 bytes per lane);
+//   gradient waves (KW .. 2KW-1) hold the dK^T and dV^T accumulators of the
+//                  same keys; one item later they read P and dS back and
+//                  accumulate dV^T += dO^T P and dK^T += Q^T dS, with dO^T and
+//                  Q^T read transposed from the item's tiles.
+// Score wave k and gradient wave KW + k share a SIMD.  Each item takes two
+// barriers: before the first the score waves run their MFMAs while the
+// gradient waves fetch P and dS; after it the gradient waves run their MFMAs
+// while the score waves do the exponentials.  So the matrix core of every SIMD
+// always has one wave feeding it, and the vector work hides behind it.
+// Q/dO tiles rotate through three LDS slots (the item being scored, the item
+// being accumulated, and the next item's loads in flight); P/dS need one
+// buffer, read before the first barrier and written after it.
+// ---------------------------------------------------------------------------
+template <int D, int BMQ>
+struct DkdvWsLayout {
+  static constexpr int KW = 4;                      // key blocks (32 keys) per workgroup
+  static constexpr int NW = 2 * KW;                 // waves per workgroup
+  static constexpr int BNK = 32 * KW;               // keys per workgroup
+  static constexpr int TILE = BMQ * D;              // elements of one Q or dO tile
+  static constexpr int SLOT = 2 * TILE * 2;         // bytes of one Q + dO slot
+  static constexpr int NSLOT = 3;
+  static constexpr int IMG = (BMQ / 16) * 64 * 16;  // bytes of one wave's P (or dS) operands
+  static constexpr int RST = 2 * BMQ * 4;           // lse2[BMQ] then dsum[BMQ]
+  static constexpr int OFF_PDS = NSLOT * SLOT;
+  static constexpr int OFF_RST = OFF_PDS + KW * 2 * IMG;
+  static constexpr int BYTES = OFF_RST + NSLOT * RST;
+};
+
+// Workgroup barrier that publishes LDS written by ds_write only: this wave's
+// LDS accesses are complete when it arrives, while its direct-to-LDS global
+// loads may stay in flight (a fence would wait for those too).  The signal
+// fences keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left open
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <class T, int D, int BMQ>
+struct DkdvWs {
+  using L = DkdvWsLayout<D, BMQ>;
+  char* smem;  // [slot][Q tile, dO tile], [score wave][P, dS images], [slot][lse2, dsum]
+  const AttnArgs* a;
+  int b, hk, k0, k_last, key, qt_lo, n_qt, n_items, wave, kb, lane, hf, nq_pad;
+  float c;
+  SwzOffsets<D> off;
+  // The score waves issue every tile load.  (A wave whose transposing LDS
+  // reads follow its own direct-to-LDS loads in program order is made to wait
+  // for those loads by the compiler, even where they cannot overlap; the
+  // score waves read LDS only with plain reads, which the compiler orders by
+  // the explicit waits and barriers here.)
+  DmaTile<D, BMQ, L::KW> qd, dd;
+
+  // Work items run over query tiles from the last one down, with the heads of
+  // the group innermost: the workgroups of one K/V head that run at the same
+  // time read the same Q/dO tiles at about the same time, and those come from
+  // L2.  Cursor (tile from the top, head) of an item:
+  struct Cursor {
+    int t, g;
+    __device__ __forceinline__ void next(int G) {
+      if (++g == G) {
+        g = 0;
+        ++t;
+      }
+    }
+  };
+  __device__ __forceinline__ int row_of(const Cursor& cu) const { return (qt_lo + n_qt - 1 - cu.t) * BMQ; }
+
+  __device__ __forceinline__ char* slot_tiles(int slot) const { return smem + slot * L::SLOT; }
+  __device__ __forceinline__ char* slot_stats(int slot) const { return smem + L::OFF_RST + slot * L::RST; }
+
+  // Score wave kb loads its share of one item's Q and dO tiles (and wave
+  // KW-1 the item's row statistics) into slot `slot`.
+  __device__ __forceinline__ void issue(const Cursor& cu, int slot) {
+    const int i0 = row_of(cu), hq = hk * a->G + cu.g;
+    qd.issue(static_cast<const uint16_t*>(a->q) + b * a->q_sb + hq * a->q_sh, a->q_sn, i0, a->Nq,
+             reinterpret_cast<uint16_t*>(slot_tiles(slot)), kb);
+    dd.issue(static_cast<const uint16_t*>(a->dout) + b * a->o_sb + hq * a->o_sh, a->o_sn, i0, a->Nq,
+             reinterpret_cast<uint16_t*>(slot_tiles(slot) + L::TILE * 2), kb);
+    if (kb == L::KW - 1) {
+      const int64_t ro = ((int64_t)b * a->Hq + hq) * nq_pad + i0;
+      uint16_t* r = reinterpret_cast<uint16_t*>(slot_stats(slot));
+      if (lane < BMQ / 4) {
+        dma16(a->lse2 + ro + 4 * lane, r);
+      } else if (lane < BMQ / 2) {
+        dma16(a->dsum + ro + 4 * (lane - BMQ / 4), r);
+      }
+    }
+  }
+
+  __device__ __forceinline__ char* img(int which) const {
+    return smem + L::OFF_PDS + (kb * 2 + which) * L::IMG + lane * 16;
+  }
+
+  // S = Q K^T and dP = dO V^T of one item, 16 d-columns (one step st) at a
+  // time; the row chunks of step st + NB - 1 are read while the MFMAs of step
+  // st run.  mid() runs once the MFMAs of the first two steps are issued.
+  template <class Mid>
+  __device__ __forceinline__ void score_products(const char* Qs, const char* dOs, const u32x4 (&kf)[D / 16],
+                                                 const u32x4 (&vf)[D / 16], f32x16 (&s)[BMQ / 32],
+                                                 f32x16 (&dp)[BMQ / 32], Mid&& mid) {
+    constexpr int NST = D / 16, NB = 3;
+    u32x4 qo[NB][BMQ / 32], go[NB][BMQ / 32];
+#pragma unroll
+    for (int qb = 0; qb < BMQ / 32; ++qb) s[qb] = dp[qb] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < NB - 1; ++st) {
+#pragma unroll
+      for (int qb = 0; qb < BMQ / 32; ++qb) {
+        qo[st][qb] = off.row_chunk(Qs, qb, st);
+        go[st][qb] = off.row_chunk(dOs, qb, st);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      if (st + NB - 1 < NST) {
+#pragma unroll
+        for (int qb = 0; qb < BMQ / 32; ++qb) {
+          qo[(st + NB - 1) % NB][qb] = off.row_chunk(Qs, qb, st + NB - 1);
+          go[(st + NB - 1) % NB][qb] = off.row_chunk(dOs, qb, st + NB - 1);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int qb = 0; qb < BMQ / 32; ++qb) {
+        s[qb] = T::mfma(qo[st % NB][qb], kf[st], s[qb]);
+        dp[qb] = T::mfma(go[st % NB][qb], vf[st], dp[qb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (st == 1) mid();
+    }
+  }
+
+  // dV^T += dO^T P and dK^T += Q^T dS over the (16-query step si, 32-column
+  // block db) pairs of one item; the transposed operands of pair p + NB - 1
+  // are read while the MFMAs of pair p run.
+  __device__ __forceinline__ void grad_products(const char* Qs, const char* dOs, const u32x4 (&pf)[BMQ / 16],
+                                                const u32x4 (&dsf)[BMQ / 16], f32x16 (&dka)[D / 32],
+                                                f32x16 (&dva)[D / 32]) {
+    constexpr int NDB = D / 32, NP = (BMQ / 16) * NDB, NB = 4;
+    static_assert(NP >= NB, "pairs");
+    u32x4 ao[NB], aq[NB];
+#pragma unroll
+    for (int pr = 0; pr < NB - 1; ++pr) {
+      ao[pr] = off.tr_operand(dOs, pr / NDB, pr % NDB);
+      aq[pr] = off.tr_operand(Qs, pr / NDB, pr % NDB);
+    }
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      if (pr + NB - 1 < NP) {
+        const int nx = pr + NB - 1;
+        ao[nx % NB] = off.tr_operand(dOs, nx / NDB, nx % NDB);
+        aq[nx % NB] = off.tr_operand(Qs, nx / NDB, nx % NDB);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int si = pr / NDB, db = pr % NDB;
+      dva[db] = T::mfma(ao[pr % NB], pf[si], dva[db]);
+      dka[db] = T::mfma(aq[pr % NB], dsf[si], dka[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // One item of a score wave: item w (if w < n_items) sits in slot `slot`;
+  // item w + 1 (cursor nx) is loaded into slot `nslot` meanwhile.
+  __device__ __forceinline__ void score_step(int w, int slot, int nslot, Cursor& cu, Cursor& nx,
+                                             const u32x4 (&kf)[D / 16], const u32x4 (&vf)[D / 16]) {
+    // [qb][r] is query i0 + 32*qb + 8*(r/4) + 4*hf + r%4.
+    f32x16 s[BMQ / 32], dp[BMQ / 32];
+    auto load_next = [&]() {
+      if (w + 1 < n_items) issue(nx, nslot);
+    };
+    if (w < n_items) {
+      score_products(slot_tiles(slot), slot_tiles(slot) + L::TILE * 2, kf, vf, s, dp, load_next);
+    } else {
+      load_next();
+    }
+    lds_barrier();  // the gradient waves have taken the previous item's P and dS
+    if (w < n_items) {
+      const int i0 = row_of(cu);
+      const int i_end = min(i0 + BMQ, a->Nq) - 1;
+      const bool full = (key_lo(*a, i_end) <= k0) && (key_hi(*a, i0) >= k_last);
+      if (!full) {
+#pragma unroll
+        for (int qb = 0; qb < BMQ / 32; ++qb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = i0 + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key < key_lo(*a, i) || key > key_hi(*a, i)) s[qb][r] = -INFINITY;
+          }
+        }
+      }
+      const float* lse2s = reinterpret_cast<const float*>(slot_stats(slot));
+      const float* dsums = lse2s + BMQ;
+      char* pimg = img(0);
+      char* dimg = img(1);
+#pragma unroll
+      for (int qb = 0; qb < BMQ / 32; ++qb) {
+        f32x4 l4[4], d4[4];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          l4[g4] = *reinterpret_cast<const f32x4*>(lse2s + 32 * qb + 8 * g4 + 4 * hf);
+          d4[g4] = *reinterpret_cast<const f32x4*>(dsums + 32 * qb + 8 * g4 + 4 * hf);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          float pb[8], db_[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * tt + e;
+            const float pr = fast_exp2(fmaf(s[qb][r], c, -l4[r >> 2][r & 3]));
+            pb[e] = pr;
+            db_[e] = pr * (dp[qb][r] - d4[r >> 2][r & 3]);
+          }
+          const int si = 2 * qb + tt;
+          *reinterpret_cast<u32x4*>(pimg + si * 1024) =
+              u32x4{T::pack(pb[0], pb[1]), T::pack(pb[2], pb[3]), T::pack(pb[4], pb[5]), T::pack(pb[6], pb[7])};
+          *reinterpret_cast<u32x4*>(dimg + si * 1024) = u32x4{T::pack(db_[0], db_[1]), T::pack(db_[2], db_[3]),
+                                                              T::pack(db_[4], db_[5]), T::pack(db_[6], db_[7])};
+        }
+      }
+    }
+    wait_all_loads();  // this wave's share of item w + 1 has landed
+    lds_barrier();     // P/dS of item w written; item w + 1 loaded
+    cu.next(a->G);
+    nx.next(a->G);
+  }
+
+  // One item of a gradient wave: accumulate item w - 1 (slot `pslot`).
+  __device__ __forceinline__ void grad_step(int w, int pslot, f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
+    u32x4 pf[BMQ / 16], dsf[BMQ / 16];
+    if (w >= 1) {
+      const char* pimg = img(0);
+      const char* dimg = img(1);
+#pragma unroll
+      for (int si = 0; si < BMQ / 16; ++si) {
+        pf[si] = *reinterpret_cast<const u32x4*>(pimg + si * 1024);
+        dsf[si] = *reinterpret_cast<const u32x4*>(dimg + si * 1024);
+      }
+    }
+    lds_barrier();  // P/dS of item w - 1 are in registers
+    if (w >= 1) grad_products(slot_tiles(pslot), slot_tiles(pslot) + L::TILE * 2, pf, dsf, dka, dva);
+    lds_barrier();
+  }
+
+  __device__ __forceinline__ void score_loop() {
+    u32x4 kf[D / 16], vf[D / 16];
+    const uint16_t* Kp = static_cast<const uint16_t*>(a->k) + b * a->k_sb + hk * a->k_sh;
+    const uint16_t* Vp = static_cast<const uint16_t*>(a->v) + b * a->v_sb + hk * a->v_sh;
+    if (key < a->Nk) {
+      const uint16_t* kr = Kp + (int64_t)key * a->k_sn + 8 * hf;
+      const uint16_t* vr = Vp + (int64_t)key * a->v_sn + 8 * hf;
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        kf[st] = *reinterpret_cast<const u32x4*>(kr + 16 * st);
+        vf[st] = *reinterpret_cast<const u32x4*>(vr + 16 * st);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) kf[st] = vf[st] = u32x4{0u, 0u, 0u, 0u};
+    }
+    Cursor cu{0, 0}, nx{0, 0};
+    nx.next(a->G);  // cursor of item w + 1
+    int slot = 0;
+    for (int w = 0; w <= n_items; ++w) {
+      const int nslot = (slot == L::NSLOT - 1) ? 0 : slot + 1;
+      score_step(w, slot, nslot, cu, nx, kf, vf);
+      slot = nslot;
+    }
+  }
+
+  __device__ __forceinline__ void grad_loop(f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dka[db] = dva[db] = f32x16{};
+    int pslot = L::NSLOT - 1;  // slot of item w - 1
+    for (int w = 0; w <= n_items; ++w) {
+      grad_step(w, pslot, dka, dva);
+      pslot = (pslot == L::NSLOT - 1) ? 0 : pslot + 1;
+    }
+  }
+};
+
+template <class T, int D, int BMQ>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_ws_kernel(AttnArgs a) {
+  using L = DkdvWsLayout<D, BMQ>;
+  static_assert(L::NW * 64 == 512, "launch bounds assume 8 waves");
+  static_assert(BMQ <= 128 && 128 % BMQ == 0, "row statistics are padded to 128 rows");
+  __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n_kt = (a.Nk + L::BNK - 1) / L::BNK;
+  // Under a causal mask the first key tiles see the most queries: run them first.
+  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_kt, 1, false, a.xcd_remap);
+
+  DkdvWs<T, D, BMQ> x;
+  x.smem = smem;
+  x.a = &a;
+  x.b = it.unit / a.Hkv;
+  x.hk = it.unit % a.Hkv;
+  x.k0 = it.tile * L::BNK;
+  x.wave = wave;
+  x.kb = wave % L::KW;
+  x.lane = lane;
+  x.hf = lane >> 5;
+  x.key = x.k0 + x.kb * 32 + (lane & 31);  // this lane's key (accumulator column)
+  x.c = a.scale_log2;
+  x.nq_pad = (a.Nq + 127) / 128 * 128;
+  x.k_last = min(x.k0 + L::BNK, a.Nk) - 1;
+  const int i_lo = query_lo(a, x.k0), i_hi = query_hi(a, x.k_last);
+  x.qt_lo = i_lo / BMQ;
+  x.n_qt = (i_hi >= i_lo) ? i_hi / BMQ - x.qt_lo + 1 : 0;
+  x.n_items = x.n_qt * a.G;  // (query tile, query head of the group) pairs
+  x.off.init(lane);
+  x.qd.init(x.kb, lane, a.q_sn);
+  x.dd.init(x.kb, lane, a.o_sn);
+
+  if (x.n_items > 0 && wave < L::KW) {
+    x.issue(typename DkdvWs<T, D, BMQ>::Cursor{0, 0}, 0);
+    wait_all_loads();
+  }
+  __syncthreads();
+  if (wave < L::KW) {
+    x.score_loop();
+    return;
+  }
+  f32x16 dka[D / 32], dva[D / 32];
+  x.grad_loop(dka, dva);
+
+  // Store dK = scale * dK and dV: lane holds d rows 32*db + 8*g4 + 4*hf + 0..3.
+  if (x.key < a.Nk) {
+    uint16_t* dkp = static_cast<uint16_t*>(a.dk) + x.b * a.k_sb + x.hk * a.k_sh + (int64_t)x.key * a.k_sn;
+    uint16_t* dvp = static_cast<uint16_t*>(a.dv) + x.b * a.v_sb + x.hk * a.v_sh + (int64_t)x.key * a.v_sn;
+    const float sc = a.scale;
+    const int hf = x.hf;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * hf;
+        *reinterpret_cast<u32x2*>(dkp + d0) =
+            u32x2{T::pack(dka[db][4 * g4] * sc, dka[db][4 * g4 + 1] * sc),
+                  T::pack(dka[db][4 * g4 + 2] * sc, dka[db][4 * g4 + 3] * sc)};
+        *reinterpret_cast<u32x2*>(dvp + d0) =
+            u32x2{T::pack(dva[db][4 * g4], dva[db][4 * g4 + 1]), T::pack(dva[db][4 * g4 + 2], dva[db][4 * g4 + 3])};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
 template <class T, int D, int BN, int NW>
@@ -553,6 +916,17 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream, int stages
   }
   AttnArgs args = a;
   args.xcd_remap = a.xcd_remap && ((a.B * a.Hkv) % 8 == 0);
+#if FA_DKDV_WS
+  using WL = DkdvWsLayout<D, FA_DKDV_BMQ>;
+  const int n_kt = (a.Nk + WL::BNK - 1) / WL::BNK;
+  const int64_t grid_kv = (int64_t)a.B * a.Hkv * n_kt;
+  if (grid_kv > 0 && (stages & kStageDkdv)) {
+    hipLaunchKernelGGL((bwd_dkdv_ws_kernel<T, D, FA_DKDV_BMQ>), dim3((unsigned)grid_kv), dim3(WL::NW * 64), 0,
+                       stream, args);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+#else
   const int n_kt = (a.Nk + FA_DKDV_NW * 32 - 1) / (FA_DKDV_NW * 32);
   const int64_t grid_kv = (int64_t)a.B * a.Hkv * n_kt;
   if (grid_kv > 0 && (stages & kStageDkdv)) {
@@ -561,6 +935,7 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream, int stages
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+#endif
   const int n_qt = (a.Nq + FA_DQ_NW * 32 - 1) / (FA_DQ_NW * 32);
   const int64_t grid_q = (int64_t)a.B * a.Hkv * n_qt * a.G;
   if (grid_q > 0 && (stages & kStageDq)) {
