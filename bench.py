@@ -110,7 +110,7 @@ def kernel_table(w, f_fwd, f_bwd, ms):
     rows_pad = w.batch * w.nheads_q * (-(-w.seqlen // 128) * 128)
     prep_bytes = 2 * rows * w.headdim * e + 4 * rows + 2 * 4 * rows_pad
     spec = [
-        ("fwd_mfma_kernel<BF16,128,64,8> (fa_fwd)", "mfma", f_fwd),
+        ("fwd_pp_kernel<BF16,128,64> (fa_fwd)", "mfma", f_fwd),
         ("bwd_preprocess_kernel<2> (fa_bwd_stage PREPARE)", "hbm", prep_bytes),
         ("bwd_dkdv_ws_kernel<BF16,128,64> (fa_bwd_stage DKDV)", "mfma", 0.8 * f_bwd),
         ("bwd_dq_kernel<BF16,128,64,8> (fa_bwd_stage DQ)", "mfma", 0.2 * f_bwd),

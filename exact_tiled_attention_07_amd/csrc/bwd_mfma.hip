@@ -417,17 +417,6 @@ struct DkdvWsLayout {
   static constexpr int BYTES = OFF_RST + NSLOT * RST;
 };
 
-// Workgroup barrier that publishes LDS written by ds_write only: this wave's
-// LDS accesses are complete when it arrives, while its direct-to-LDS global
-// loads may stay in flight (a fence would wait for those too).  The signal
-// fences keep the compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left open
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 template <class T, int D, int BMQ>
 struct DkdvWs {
   using L = DkdvWsLayout<D, BMQ>;

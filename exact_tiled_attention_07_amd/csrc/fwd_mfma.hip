@@ -7,23 +7,22 @@
 // that the full score matrix never exists.  The output is the exact attention
 // result; the kernel also writes the per-row log-sum-exp for the backward pass.
 //
-// gfx950 mapping.  One workgroup = NW waves = a tile of BM = 32*NW queries of
-// one (batch, query head); each wave owns 32 query rows.  For every K/V tile of
+// gfx950 mapping.  One workgroup = 8 waves = a tile of 256 queries of one
+// (batch, query head); each wave owns 32 query rows.  For every K/V tile of
 // BN keys:
 //   S^T (BN x 32) = K Q^T      A operand = K rows from LDS, B = Q (registers)
 //   online softmax             lane l holds query l%32 and 16 keys per 32x32
 //                              block, so row max/sum are in-register plus one
 //                              exchange with lane l^32
-//   O^T (D x 32) += V^T P^T    A operand = V^T from a transposed LDS copy,
-//                              B = P^T straight from the softmax registers
+//   O^T (D x 32) += V^T P^T    A operand = V^T read transposed from the
+//                              row-major V tile, B = P^T from the softmax
 // The O rescale by exp(m_old - m_new) is a per-lane scalar (one query per lane).
 // Scores are kept in raw units; exp(scale*(s - m)) is evaluated as
 // exp2(s*c - m*c) with c = scale*log2(e), one FMA and one v_exp_f32.
-// K and V tiles sit in LDS row-major with a chunk swizzle (tile_io.hpp); V^T
-// operands come straight from the row-major tile through the transposing LDS
-// read.  Tiles are double buffered: each step first issues the direct-to-LDS
-// loads of tile t+1 into the other buffer, then computes tile t; one barrier
-// per tile.
+// K and V tiles sit in LDS row-major with a chunk swizzle (tile_io.hpp) and
+// arrive by direct-to-LDS loads.  The two halves of the workgroup alternate
+// between matrix products and softmax (below), so that on every SIMD one wave
+// keeps the matrix core busy while the other does the vector work.
 #include <type_traits>
 
 #include "common.hpp"
@@ -42,61 +41,108 @@ static constexpr float kLazyRescale = 8.0f;
 #ifndef FA_FWD_BN
 #define FA_FWD_BN 64  // keys per K/V tile
 #endif
-#ifndef FA_FWD_NW
-#define FA_FWD_NW 8  // waves per workgroup (32 queries each)
-#endif
-#ifndef FA_FWD_WPE
-#define FA_FWD_WPE 2  // waves per SIMD the register allocation targets
-#endif
-#ifndef FA_FWD_PRIO
-#define FA_FWD_PRIO 0  // raise wave priority around MFMA phases (measured: no gain)
+#ifndef FA_FWD_RING
+#define FA_FWD_RING 3  // LDS operands in flight ahead of the MFMA that uses them
 #endif
 
-// Per-workgroup state of the forward kernel; step<BUF>() processes one K/V tile
-// held in LDS buffer BUF while the next tile is loaded into the other buffer.
-template <class T, int D, int BN, int NW>
-struct FwdCtx {
+// ---------------------------------------------------------------------------
+// Forward with two wave groups in ping-pong.
+//
+// Waves 0-3 (group A) and 4-7 (group B) each own 32 queries; waves w and w+4
+// share a SIMD.  Per K/V tile m the work of a wave is an MFMA interval
+// (O += V(m-1)^T P(m-1)^T, then S(m) = K(m) Q^T)
+// and a softmax interval (mask, row max, lazy rescale, P = exp2(...)).
+// Group B runs half a tile behind group A, with a barrier between intervals:
+//     interval 2m:    A  MFMA(m)        B  softmax(m-1)
+//     interval 2m+1:  A  softmax(m)     B  MFMA(m)
+// so on every SIMD one wave feeds the matrix core while the other does the
+// softmax.  K(m) is read in intervals 2m and 2m+1, V(m) in 2m+2 and 2m+3,
+// each from two LDS buffers.  Group A loads K(m+1) and V(m) at the end of
+// its MFMA interval 2m (after its last transposing read of the interval,
+// which the compiler would otherwise hold for the loads), into the buffers
+// whose last readers finished in interval 2m-1, and waits for them at the
+// end of interval 2m+1.
+// ---------------------------------------------------------------------------
+template <class T, int D, int BN>
+struct FwdPP {
+  static constexpr int NW = 8, HALF = 4;
   static constexpr int TILE = BN * D;  // elements of one K or V tile
-  uint16_t* smem;                      // [buf][K tile, V tile], swizzled row-major
+  uint16_t* kbuf;                      // [2][TILE], swizzled row-major
+  uint16_t* vbuf;                      // [2][TILE]
   const uint16_t* Kp;
   const uint16_t* Vp;
   int64_t k_sn, v_sn;
-  int Nk, t_hi, lo_i, hi_i, lo_max, hi_min, wave, lane, hf;
+  int Nk, t_lo, n, lo_i, hi_i, lo_max, hi_min, wave, lane, hf;
   float c;
   u32x4 qf[D / 16];
   int kro[D / 16];     // per-lane LDS offsets of the K row chunks
   int vro[D / 32][2];  // per-lane LDS offsets of the transposing V reads
-  DmaTile<D, BN, NW> kd, vd;
+  DmaTile<D, BN, HALF> kd, vd;  // group A's shares of the K and V tile loads
   float mref, l;
   f32x16 oacc[D / 32];
+  f32x16 s[BN / 32];  // scores of tile m between its MFMA and softmax intervals
+  u32x4 pf[BN / 16];  // P^T of tile m between its softmax and the next MFMA interval
 
-  template <int BUF>
-  __device__ __forceinline__ void step(int t) {
-    const char* Ks = reinterpret_cast<const char*>(smem + BUF * 2 * TILE);
-    const char* Vs = Ks + TILE * 2;
-    const int j0 = t * BN;
-    if (t < t_hi) {
-      kd.issue(Kp, k_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE, wave);
-      vd.issue(Vp, v_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE + TILE, wave);
+  static constexpr int NPV = (BN / 16) * (D / 32), NS = (D / 16) * (BN / 32);
+
+  // Operand o of an MFMA interval: o < NPV are the V^T operands of
+  // O^T += V^T P^T (16-key step si = o / (D/32), column block db = o % (D/32)),
+  // read transposed from the row-major V tile; the rest are the K row chunks
+  // of S^T = K Q^T (step st, key block kb).
+  __device__ __forceinline__ u32x4 operand(const char* Vs, const char* Ks, int o) const {
+    if (o < NPV) {
+      const int si = o / (D / 32), db = o % (D / 32);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + si * 16 * 2 * D + vro[db][0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Vs + si * 16 * 2 * D + vro[db][1]));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{l2[0], l2[1], h2[0], h2[1]};
     }
+    const int st = (o - NPV) / (BN / 32), kb = (o - NPV) % (BN / 32);
+    return *reinterpret_cast<const u32x4*>(Ks + kb * 32 * 2 * D + kro[st]);
+  }
 
-    // S^T = K Q^T.  s[kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
-    // MFMA phases run at raised wave priority so that, of the waves sharing a
-    // SIMD, the one feeding the matrix core issues first and the other fills
-    // the VALU with softmax work.
-    f32x16 s[BN / 32];
+  // MFMA interval of tile m (relative to t_lo); PAR = m & 1.  Every interval
+  // runs both products: in interval 0 there is no tile -1, and P^T and the V
+  // buffer it reads start as zeros, so that product adds 0; after the last
+  // tile the S product reads a stale K buffer and its result is never used.
+  // Each LDS operand is read NB - 1 MFMAs ahead of its use.
+  // s[kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
+  template <int PAR>
+  __device__ __forceinline__ void mfma_interval(int m, bool group_a) {
+    constexpr int NB = FA_FWD_RING, NO = NPV + NS;
+    static_assert(NPV >= NB, "interval shape");
+    const char* Vs = reinterpret_cast<const char*>(vbuf + (1 - PAR) * TILE);
+    const char* Ks = reinterpret_cast<const char*>(kbuf + PAR * TILE);
+    u32x4 ring[NB];
+#pragma unroll
+    for (int o = 0; o < NB - 1; ++o) ring[o % NB] = operand(Vs, Ks, o);
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
-    if (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-        s[kb] = T::mfma(*reinterpret_cast<const u32x4*>(Ks + kb * 32 * 2 * D + kro[st]), qf[st], s[kb]);
+    for (int o = 0; o < NO; ++o) {
+      if (o + NB - 1 < NO) ring[(o + NB - 1) % NB] = operand(Vs, Ks, o + NB - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (o < NPV) {
+        const int si = o / (D / 32), db = o % (D / 32);
+        oacc[db] = T::mfma(ring[o % NB], pf[si], oacc[db]);
+      } else {
+        const int st = (o - NPV) / (BN / 32), kb = (o - NPV) % (BN / 32);
+        s[kb] = T::mfma(ring[o % NB], qf[st], s[kb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
+    // Group A's tile loads, after the last transposing read of the interval
+    // (issued in one burst: spread between the S products they stall them).
+    if (group_a) {
+      if (m + 1 < n) kd.issue(Kp, k_sn, (t_lo + m + 1) * BN, Nk, kbuf + (1 - PAR) * TILE, wave);
+      if (m < n) vd.issue(Vp, v_sn, (t_lo + m) * BN, Nk, vbuf + PAR * TILE, wave);
+    }
+  }
 
-    // Causal / window / sequence-end masking, only on tiles that need it.
+  // Softmax interval of tile m: mask, row max, lazy rescale of O and l, P.
+  __device__ __forceinline__ void softmax_interval(int m) {
+    if (m < 0 || m >= n) return;
+    const int j0 = (t_lo + m) * BN;
     const bool full = (j0 >= lo_max) && (j0 + BN - 1 <= hi_min);
     if (!full) {
 #pragma unroll
@@ -108,9 +154,9 @@ struct FwdCtx {
         }
       }
     }
-
-    // Online softmax.  The reference maximum moves only when some row of the
-    // wave grew by more than 2^kLazyRescale; then O and l are rescaled.
+    // The reference maximum moves only when some row of the wave grew by more
+    // than 2^kLazyRescale; then O and l (which hold the tiles up to m - 1) are
+    // rescaled.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
@@ -127,7 +173,6 @@ struct FwdCtx {
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
     }
     const float mc = (mref == -INFINITY) ? 0.f : mref * c;
-    u32x4 pf[BN / 16];  // P^T as B operands, one per 16 keys
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
@@ -138,43 +183,24 @@ struct FwdCtx {
           p[e] = fast_exp2(fmaf(s[kb][8 * tt + e], c, -mc));
           l += p[e];
         }
-        pf[2 * kb + tt] = u32x4{T::pack(p[0], p[1]), T::pack(p[2], p[3]), T::pack(p[4], p[5]),
-                                T::pack(p[6], p[7])};
+        pf[2 * kb + tt] = u32x4{T::pack(p[0], p[1]), T::pack(p[2], p[3]), T::pack(p[4], p[5]), T::pack(p[6], p[7])};
       }
     }
-
-    // O^T += V^T P^T, V^T read transposed from the row-major tile.
-    if (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int si = 0; si < BN / 16; ++si) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(Vs + si * 16 * 2 * D + vro[db][0]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(Vs + si * 16 * 2 * D + vro[db][1]));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        oacc[db] = T::mfma(u32x4{l2[0], l2[1], h2[0], h2[1]}, pf[si], oacc[db]);
-      }
-    }
-    if (FA_FWD_PRIO) __builtin_amdgcn_s_setprio(0);
-    wait_all_loads();  // the next tile has landed in this wave's share of LDS
-    __syncthreads();
   }
 };
 
-template <class T, int D, int BN, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_FWD_WPE, FA_FWD_WPE))) void fwd_mfma_kernel(AttnArgs a) {
-  constexpr int BM = NW * 32;
-  using Ctx = FwdCtx<T, D, BN, NW>;
-  constexpr int TILE = Ctx::TILE;
-  // Two buffers, each one K tile then one V tile, filled by direct-to-LDS loads.
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];
-  static_assert(2 * 2 * TILE * 2 <= 65536, "LDS offsets must fit the 16-bit immediate");
+template <class T, int D, int BN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pp_kernel(AttnArgs a) {
+  using Ctx = FwdPP<T, D, BN>;
+  constexpr int NW = Ctx::NW, BM = NW * 32, TILE = Ctx::TILE;
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[2 * TILE];
+  static_assert(2 * TILE * 2 <= 65536, "LDS offsets of one buffer pair must fit the 16-bit immediate");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
+  const bool group_a = wave < Ctx::HALF;
 
   const int n_qt = (a.Nq + BM - 1) / BM;
   const bool heavy_last = (a.causal || a.wr >= 0) && a.wl < 0;
@@ -185,7 +211,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_FWD_
   const int qrow = q0 + wave * 32 + l32;  // the query of this lane's column
 
   Ctx x;
-  x.smem = smem;
+  x.kbuf = kbuf;
+  x.vbuf = vbuf;
   x.Kp = static_cast<const uint16_t*>(a.k) + b * a.k_sb + hk * a.k_sh;
   x.Vp = static_cast<const uint16_t*>(a.v) + b * a.v_sb + hk * a.v_sh;
   x.k_sn = a.k_sn;
@@ -207,18 +234,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_FWD_
     for (int st = 0; st < D / 16; ++st) x.qf[st] = u32x4{0u, 0u, 0u, 0u};
   }
 
-  // Visible keys of this lane's query, and the workgroup's key range.
+  // Visible keys of this lane's query, and the workgroup's key tiles.
   x.lo_i = key_lo(a, qrow);
   x.hi_i = key_hi(a, qrow);
   const int q_last = min(q0 + BM, a.Nq) - 1;
   const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
   x.lo_max = key_lo(a, q_last);
   x.hi_min = key_hi(a, q0);
-  const int t_lo = kv_lo / BN;
-  x.t_hi = (kv_hi >= kv_lo) ? kv_hi / BN : t_lo - 1;
+  x.t_lo = kv_lo / BN;
+  x.n = (kv_hi >= kv_lo) ? kv_hi / BN - x.t_lo + 1 : 0;
 
-  // Per-lane LDS byte offsets, fixed for the whole kernel; tile, buffer,
-  // key-block and 16-key-step offsets are compile-time immediates.
+  // Per-lane LDS byte offsets, fixed for the whole kernel.
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) x.kro[st] = Swz<D>::off(l32, 2 * st + hf);
   {
@@ -236,22 +262,63 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_FWD_
   x.l = 0.f;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) x.oacc[db] = f32x16{};
+#pragma unroll
+  for (int si = 0; si < BN / 16; ++si) x.pf[si] = u32x4{0u, 0u, 0u, 0u};
+  // V buffer 1 is first loaded for tile 1; interval 0's product reads it as zeros.
+  static_assert((TILE * 2) % (512 * 16) == 0, "V buffer clears in 16-byte stores");
+#pragma unroll
+  for (int i = 0; i < TILE * 2 / (512 * 16); ++i)
+    reinterpret_cast<u32x4*>(vbuf + TILE)[i * 512 + tid] = u32x4{0u, 0u, 0u, 0u};
 
   x.kd.init(wave, lane, a.k_sn);
   x.vd.init(wave, lane, a.v_sn);
-  if (t_lo <= x.t_hi) {
-    x.kd.issue(x.Kp, a.k_sn, t_lo * BN, a.Nk, smem, wave);
-    x.vd.issue(x.Vp, a.v_sn, t_lo * BN, a.Nk, smem + TILE, wave);
+  if (group_a && x.n > 0) {
+    x.kd.issue(x.Kp, a.k_sn, x.t_lo * BN, a.Nk, kbuf, wave);
     wait_all_loads();
   }
   __syncthreads();
 
-  int t = t_lo;
-  for (; t + 1 <= x.t_hi; t += 2) {
-    x.template step<0>(t);
-    x.template step<1>(t + 1);
+  // 2(n+1) intervals; both groups pass the same barriers.
+  const int n = x.n;
+  int m = 0;
+  if (group_a) {
+    for (; m + 1 <= n; m += 2) {
+      x.template mfma_interval<0>(m, true);
+      lds_barrier();
+      x.softmax_interval(m);
+      wait_all_loads();
+      lds_barrier();
+      x.template mfma_interval<1>(m + 1, true);
+      lds_barrier();
+      x.softmax_interval(m + 1);
+      wait_all_loads();
+      lds_barrier();
+    }
+    if (m <= n) {
+      x.template mfma_interval<0>(m, true);
+      lds_barrier();
+      x.softmax_interval(m);
+      wait_all_loads();
+      lds_barrier();
+    }
+  } else {
+    for (; m + 1 <= n; m += 2) {
+      x.softmax_interval(m - 1);
+      lds_barrier();
+      x.template mfma_interval<0>(m, false);
+      lds_barrier();
+      x.softmax_interval(m);
+      lds_barrier();
+      x.template mfma_interval<1>(m + 1, false);
+      lds_barrier();
+    }
+    if (m <= n) {
+      x.softmax_interval(m - 1);
+      lds_barrier();
+      x.template mfma_interval<0>(m, false);
+      lds_barrier();
+    }
   }
-  if (t <= x.t_hi) x.template step<0>(t);
 
   // Epilogue: O = O / l, LSE = scale*mref + ln(l).  Lanes l and l^32 hold
   // different keys of the same query, so their partial sums are added here.
@@ -282,18 +349,18 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t stream) {
   if (total == 0) return hipSuccess;
   AttnArgs args = a;
   args.xcd_remap = a.xcd_remap && ((a.B * a.Hkv) % 8 == 0);
-  hipLaunchKernelGGL((fwd_mfma_kernel<T, D, BN, NW>), dim3((unsigned)total), dim3(NW * 64), 0,
-                     stream, args);
+  static_assert(NW == FwdPP<T, D, BN>::NW, "the forward runs 8 waves");
+  hipLaunchKernelGGL((fwd_pp_kernel<T, D, BN>), dim3((unsigned)total), dim3(NW * 64), 0, stream, args);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t stream) {
   if (a.dtype == kBF16) {
-    if (a.D == 128) return launch_fwd_t<BF16, 128, FA_FWD_BN, FA_FWD_NW>(a, stream);
-    if (a.D == 64) return launch_fwd_t<BF16, 64, FA_FWD_BN, FA_FWD_NW>(a, stream);
+    if (a.D == 128) return launch_fwd_t<BF16, 128, FA_FWD_BN, 8>(a, stream);
+    if (a.D == 64) return launch_fwd_t<BF16, 64, FA_FWD_BN, 8>(a, stream);
   } else if (a.dtype == kF16) {
-    if (a.D == 128) return launch_fwd_t<F16, 128, FA_FWD_BN, FA_FWD_NW>(a, stream);
-    if (a.D == 64) return launch_fwd_t<F16, 64, FA_FWD_BN, FA_FWD_NW>(a, stream);
+    if (a.D == 128) return launch_fwd_t<F16, 128, FA_FWD_BN, 8>(a, stream);
+    if (a.D == 64) return launch_fwd_t<F16, 64, FA_FWD_BN, 8>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -62,7 +62,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // ===========================================================================
 // 16 bytes per lane from global memory straight into LDS at
 // lds_block + 16 * lane (lds_block must be the same for the whole wave).
-__device__ __forceinline__ void dma16(const void* g, uint16_t* lds_block) {
+// (Forcing the scalar-base form, a wave-uniform global base in SGPRs plus a
+// 32-bit lane offset and the LDS base taken from the first lane, measured
+// slower on MI355X for every kernel here.)
+__device__ __forceinline__ void dma16(const void* g, const void* lds_block) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_block, 16, 0, 0);
 }
 
@@ -113,6 +116,17 @@ struct DmaTile {
     }
   }
 };
+
+// Workgroup barrier that publishes LDS written by ds_write only: this wave's
+// LDS accesses are complete when it arrives, while its direct-to-LDS global
+// loads may stay in flight (a fence would wait for those too).  The signal
+// fences keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left open
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Wait until this wave's direct-to-LDS loads (and every other outstanding
 // memory operation of the wave) have completed.
