@@ -116,6 +116,9 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
 #ifndef FA_DKDV_WPE
 #define FA_DKDV_WPE 1
 #endif
+#ifndef FA_DQ_RING
+#define FA_DQ_RING 3  // LDS operands in flight ahead of the MFMA that uses them
+#endif
 #ifndef FA_DKDV_WS
 #define FA_DKDV_WS 1  // dK/dV with specialised score and gradient waves
 #endif
@@ -756,15 +759,28 @@ struct DqCtx {
       vd.issue(Vp, v_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE + TILE, wave);
     }
     // S^T = K Q^T and dP^T = V dO^T; element [kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
+    // Operand o: step st = o / (2 * BN/32), key block kb, K (even o) or V (odd o)
+    // row chunk; each is read NB - 1 MFMAs ahead of its use.
     f32x16 s[BN / 32], dp[BN / 32];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) s[kb] = dp[kb] = f32x16{};
+    {
+      constexpr int NB = FA_DQ_RING, NO = (D / 16) * (BN / 32) * 2;
+      auto opnd = [&](int o) {
+        const int st = o / (2 * (BN / 32)), kb = (o / 2) % (BN / 32);
+        return (o & 1) ? off.row_chunk(Vs, kb, st) : off.row_chunk(Ks, kb, st);
+      };
+      u32x4 ring[NB];
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
+      for (int o = 0; o < NB - 1; ++o) ring[o] = opnd(o);
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-        s[kb] = T::mfma(off.row_chunk(Ks, kb, st), qf[st], s[kb]);
-        dp[kb] = T::mfma(off.row_chunk(Vs, kb, st), df[st], dp[kb]);
+      for (int o = 0; o < NO; ++o) {
+        if (o + NB - 1 < NO) ring[(o + NB - 1) % NB] = opnd(o + NB - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int st = o / (2 * (BN / 32)), kb = (o / 2) % (BN / 32);
+        if (o & 1) dp[kb] = T::mfma(ring[o % NB], df[st], dp[kb]);
+        else s[kb] = T::mfma(ring[o % NB], qf[st], s[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     const bool full = (j0 >= lo_max) && (j0 + BN - 1 <= hi_min);
@@ -795,10 +811,21 @@ struct DqCtx {
                                  T::pack(ds[6], ds[7])};
       }
     }
+    {
+      constexpr int NB = FA_DQ_RING, NO = (BN / 16) * (D / 32);
+      u32x4 ring[NB];
 #pragma unroll
-    for (int si = 0; si < BN / 16; ++si) {
+      for (int o = 0; o < NB - 1; ++o) ring[o] = off.tr_operand(Ks, o / (D / 32), o % (D / 32));
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) dqa[db] = T::mfma(off.tr_operand(Ks, si, db), dsf[si], dqa[db]);
+      for (int o = 0; o < NO; ++o) {
+        if (o + NB - 1 < NO) {
+          const int nx = o + NB - 1;
+          ring[nx % NB] = off.tr_operand(Ks, nx / (D / 32), nx % (D / 32));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dqa[o % (D / 32)] = T::mfma(ring[o % NB], dsf[o / (D / 32)], dqa[o % (D / 32)]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     wait_all_loads();
     __syncthreads();
