@@ -44,7 +44,18 @@ class FaParams(ctypes.Structure):
     ]
 
 
+class FaKvParams(ctypes.Structure):
+    _fields_ = [
+        ("base", FaParams),
+        ("knew_strides", _I64x3),
+        ("vnew_strides", _I64x3),
+        ("num_splits", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 _P = ctypes.POINTER(FaParams)
+_PK = ctypes.POINTER(FaKvParams)
 _V = ctypes.c_void_p
 SIGNATURES = {
     "fa_fwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
@@ -52,6 +63,8 @@ SIGNATURES = {
     "fa_bwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "fa_bwd_stage": (ctypes.c_int, [_P, ctypes.c_int, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t,
                                     _V]),
+    "fa_fwd_kvcache_workspace_size": (ctypes.c_int, [_PK, ctypes.POINTER(ctypes.c_size_t)]),
+    "fa_fwd_kvcache": (ctypes.c_int, [_PK, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_version": (ctypes.c_int, []),
@@ -214,6 +227,67 @@ def bwd(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1), scale=No
         else:
             _check(lib.fa_bwd_stage(ctypes.byref(p), int(stage), *ptrs))
     return dq, dk, dv
+
+
+def make_kv_params(q, k_cache, v_cache, out, k_new=None, v_new=None, *, causal=False, window_size=(-1, -1),
+                   scale=None, num_splits=0):
+    """FaKvParams: q/out (B, Nq, Hq, d), caches (B, capacity, Hkv, d), new rows like q with Hkv heads."""
+    base = make_params(q, k_cache, v_cache, out, causal=causal, window_size=window_size, scale=scale)
+    p = FaKvParams()
+    p.base = base
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new must both be given or both be None")
+    if k_new is not None:
+        want = (q.shape[0], q.shape[1], k_cache.shape[2], q.shape[3])
+        for t in (k_new, v_new):
+            if tuple(t.shape) != want or t.dtype != q.dtype:
+                raise ValueError(f"k_new / v_new must be {want} of dtype {q.dtype}")
+            if t.stride(3) != 1 and t.shape[3] > 1:
+                raise ValueError("the headdim axis must be contiguous (stride 1)")
+        p.knew_strides, p.vnew_strides = _strides3(k_new), _strides3(v_new)
+    p.num_splits = int(num_splits)
+    p.reserved = 0
+    return p
+
+
+def kvcache_workspace_size(params):
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.fa_fwd_kvcache_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return n.value
+
+
+def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, *, causal=False,
+                window_size=(-1, -1), scale=None, num_splits=0, out=None, lse=None, workspace=None):
+    """Attention of q against a KV cache, appending k_new / v_new first: returns (o, lse).
+
+    q (B, Nq, Hq, d); k_cache, v_cache (B, capacity, Hkv, d), updated in place
+    when k_new / v_new (B, Nq, Hkv, d) are given; cache_seqlens int32 (B,) on the
+    device, the valid rows before the append.  Query i is aligned to key
+    i + Lk - Nq where Lk is the key count after the append.  num_splits = 0
+    lets the library choose how many parts the key range is split into.
+    """
+    _require_gpu(q, k_cache, v_cache, cache_seqlens)
+    if k_new is not None:
+        _require_gpu(k_new, v_new)
+    lib = load_library()
+    if cache_seqlens.dtype != torch.int32 or tuple(cache_seqlens.shape) != (q.shape[0],) \
+            or not cache_seqlens.is_contiguous():
+        raise ValueError("cache_seqlens must be a contiguous int32 tensor of shape (batch,)")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    p = make_kv_params(q, k_cache, v_cache, out, k_new, v_new, causal=causal, window_size=window_size,
+                       scale=scale, num_splits=num_splits)
+    need = kvcache_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_fwd_kvcache(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+                                  _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), _ptr(workspace),
+                                  workspace.numel(), _stream(q.device)))
+    return out, lse
 
 
 class _Attention(torch.autograd.Function):

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 
-SOURCES = ["fa_api.cpp", "fwd_mfma.hip", "bwd_mfma.hip", "f32_valu.hip"]
+SOURCES = ["fa_api.cpp", "fwd_mfma.hip", "bwd_mfma.hip", "f32_valu.hip", "decode.hip"]
 HEADERS = ["common.hpp", "tile_io.hpp", "launch.hpp"]
 
 ARCH = "gfx950"

@@ -132,41 +132,6 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
 #define FA_DQ_WPE 2
 #endif
 
-// Per-lane LDS byte offsets of a swizzled D-wide tile (tile_io.hpp):
-// row chunks for an operand whose lanes run along the rows (row l32 of each
-// 32-row block, chunk 2*st + hf), and the transposing reads for an operand
-// whose reduction axis runs along the rows (16-row step 0, column block db,
-// lower/upper 8 rows).  Row-block, step and buffer offsets are immediates.
-template <int D>
-struct SwzOffsets {
-  int chunk[D / 16];
-  int tr[D / 32][2];
-  __device__ __forceinline__ void init(int lane) {
-    const int l32 = lane & 31, hf = lane >> 5;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) chunk[st] = Swz<D>::off(l32, 2 * st + hf);
-    const int G = lane >> 4, j = lane & 15;
-    const int vhf = G >> 1, gsub = G & 1, ep = j >> 2, q = j & 3;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int cc = 4 * db + 2 * gsub + (q >> 1);
-      tr[db][0] = Swz<D>::off(4 * vhf + ep, cc) + 8 * (q & 1);
-      tr[db][1] = Swz<D>::off(8 + 4 * vhf + ep, cc) + 8 * (q & 1);
-    }
-  }
-  // Row chunk operand at row-block rb (32 rows) of the tile at `tile`.
-  __device__ __forceinline__ u32x4 row_chunk(const char* tile, int rb, int st) const {
-    return *reinterpret_cast<const u32x4*>(tile + rb * 32 * 2 * D + chunk[st]);
-  }
-  // Transposed operand for 16-row step si and column block db.
-  __device__ __forceinline__ u32x4 tr_operand(const char* tile, int si, int db) const {
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + si * 16 * 2 * D + tr[db][0]));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + si * 16 * 2 * D + tr[db][1]));
-    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-    return u32x4{l2[0], l2[1], h2[0], h2[1]};
-  }
-};
-
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------

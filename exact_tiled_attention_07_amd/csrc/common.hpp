@@ -49,6 +49,31 @@ struct AttnArgs {
   int32_t xcd_remap; // 1: map consecutive workgroup ids onto one XCD's work
 };
 
+// Launch arguments of attention against a KV cache (decode.hip).
+struct KvArgs {
+  const void* q;
+  void* k_cache;
+  void* v_cache;
+  const void* k_new;  // NULL: no append
+  const void* v_new;
+  void* o;
+  float* lse;                 // (B, Hq, Nq)
+  const int32_t* cache_seqlens;  // (B) device
+  float* ws_o;                // (B, Hq, Nq, S, D) partial O / l
+  float* ws_lse;              // (B, Hq, Nq, S) partial LSE
+  int64_t q_sb, q_sn, q_sh;
+  int64_t kc_sb, kc_sn, kc_sh;
+  int64_t vc_sb, vc_sn, vc_sh;
+  int64_t kn_sb, kn_sn, kn_sh;
+  int64_t vn_sb, vn_sn, vn_sh;
+  int64_t o_sb, o_sn, o_sh;
+  int32_t B, Nq, cap, Hq, Hkv, G, D, dtype;
+  float scale, scale_log2;
+  int32_t causal, wl, wr, append;
+  int32_t S;     // key-range parts per (batch, kv head, row block)
+  int32_t n_rb;  // blocks of 32 packed query rows (G * Nq rows)
+};
+
 static constexpr float kLog2e = 1.4426950408889634f;
 static constexpr float kLn2 = 0.6931471805599453f;
 

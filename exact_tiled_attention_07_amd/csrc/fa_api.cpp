@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -155,6 +156,56 @@ size_t workspace_bytes_for(const fa_params* p) {
   return ((n + 255) / 256) * 256;
 }
 
+
+// ----------------------------------------------------------------------------
+// Attention against a KV cache.
+// ----------------------------------------------------------------------------
+constexpr int64_t kMaxKvParts = 1024;
+
+fa_status check_kv_params(const fa_kvcache_params* kp) {
+  if (!kp) return fail(FA_ERR_INVALID_ARG, "params is NULL");
+  const fa_params* p = &kp->base;
+  fa_status s = check_params(p);
+  if (s != FA_OK) return s;
+  if (kp->num_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", kp->num_splits);
+  if (kp->reserved != 0) return fail(FA_ERR_INVALID_ARG, "reserved must be 0");
+  if (p->dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "fa_fwd_kvcache supports fp16 and bf16 only");
+  const int64_t* strides[2] = {kp->knew_strides, kp->vnew_strides};
+  const char* names[2] = {"knew", "vnew"};
+  for (int t = 0; t < 2; ++t) {
+    for (int i = 0; i < 3; ++i) {
+      const int64_t st = strides[t][i];
+      if (st < 0) return fail(FA_ERR_UNSUPPORTED, "%s_strides[%d] is negative", names[t], i);
+      if ((st * 2) % 16 != 0)
+        return fail(FA_ERR_UNSUPPORTED, "%s_strides[%d]=%lld is not a multiple of 16 bytes", names[t], i,
+                    (long long)st);
+    }
+  }
+  return FA_OK;
+}
+
+// Key-range parts per (batch, K/V head, block of 32 packed query rows).
+int64_t kv_parts(const fa_kvcache_params* kp) {
+  const fa_params* p = &kp->base;
+  const int64_t G = p->nheads_q / p->nheads_kv;
+  const int64_t n_rb = (G * p->seqlen_q + 31) / 32;
+  const int64_t tiles = std::max<int64_t>(1, (p->seqlen_k + 31) / 32);
+  if (kp->num_splits > 0) return std::min<int64_t>({(int64_t)kp->num_splits, tiles, kMaxKvParts});
+  // Enough single-wave parts for about two waves per SIMD of a 256-CU GPU,
+  // with at least 4 key tiles per part.
+  const int64_t units = std::max<int64_t>(1, p->batch * p->nheads_kv * n_rb);
+  int64_t s = (2048 + units - 1) / units;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 4));
+  return std::max<int64_t>(1, std::min<int64_t>(s, kMaxKvParts));
+}
+
+size_t kv_workspace_bytes(const fa_kvcache_params* kp) {
+  const fa_params* p = &kp->base;
+  const size_t rows = (size_t)p->batch * (size_t)p->nheads_q * (size_t)p->seqlen_q;
+  const size_t n = rows * (size_t)kv_parts(kp) * (size_t)(p->headdim + 1) * sizeof(float);
+  return ((n + 255) / 256) * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +308,79 @@ fa_status fa_bwd_stage(const fa_params* params, int stage, const void* dout, con
     default: return fail(FA_ERR_INVALID_ARG, "unknown backward stage %d", stage);
   }
   return run_bwd(params, mask, dout, q, k, v, o, lse, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_fwd_kvcache_workspace_size(const fa_kvcache_params* params, size_t* bytes) {
+  fa_status s = check_kv_params(params);
+  if (s != FA_OK) return s;
+  if (!bytes) return fail(FA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = kv_workspace_bytes(params);
+  return FA_OK;
+}
+
+fa_status fa_fwd_kvcache(const fa_kvcache_params* params, const void* q, void* k_cache, void* v_cache,
+                         const int32_t* cache_seqlens, const void* k_new, const void* v_new, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status s = check_kv_params(params);
+  if (s != FA_OK) return s;
+  const fa_params* p = &params->base;
+  if (p->headdim != 64 && p->headdim != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_kvcache needs headdim 64 or 128 (got %lld)", (long long)p->headdim);
+  const bool nonempty = p->batch > 0 && p->seqlen_q > 0;
+  if (!nonempty) return FA_OK;
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(FA_ERR_INVALID_ARG, "k_new and v_new must both be given or both be NULL");
+  const bool has_cache = p->seqlen_k > 0;
+  if ((s = check_ptr(q, "q", true)) != FA_OK) return s;
+  if ((s = check_ptr(k_cache, "k_cache", has_cache)) != FA_OK) return s;
+  if ((s = check_ptr(v_cache, "v_cache", has_cache)) != FA_OK) return s;
+  if ((s = check_ptr(o, "o", true)) != FA_OK) return s;
+  if ((s = check_ptr(lse, "lse", true)) != FA_OK) return s;
+  if ((s = check_ptr(k_new, "k_new", k_new != nullptr)) != FA_OK) return s;
+  if ((s = check_ptr(v_new, "v_new", v_new != nullptr)) != FA_OK) return s;
+  if (!cache_seqlens) return fail(FA_ERR_INVALID_ARG, "cache_seqlens is NULL");
+  if ((reinterpret_cast<uintptr_t>(cache_seqlens) & 3u) != 0)
+    return fail(FA_ERR_UNSUPPORTED, "cache_seqlens is not 4-byte aligned");
+  const size_t need = kv_workspace_bytes(params);
+  if ((s = check_ptr(workspace, "workspace", true)) != FA_OK) return s;
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  {
+    const void* ins[5] = {q, k_cache, v_cache, k_new, v_new};
+    for (const void* y : ins)
+      if (y && (y == o || y == lse)) return fail(FA_ERR_INVALID_ARG, "o and lse must not alias the inputs");
+  }
+  const int64_t G = p->nheads_q / p->nheads_kv;
+  const int64_t n_rb = (G * p->seqlen_q + 31) / 32;
+  const int64_t S = kv_parts(params);
+  if (p->batch * p->nheads_kv * n_rb * S >= (int64_t(1) << 31))
+    return fail(FA_ERR_UNSUPPORTED, "launch grid would exceed 2^31 workgroups");
+  if ((s = check_device()) != FA_OK) return s;
+
+  fa::KvArgs k{};
+  k.q = q; k.k_cache = k_cache; k.v_cache = v_cache; k.k_new = k_new; k.v_new = v_new;
+  k.o = o; k.lse = lse; k.cache_seqlens = cache_seqlens;
+  const size_t rows = (size_t)p->batch * (size_t)p->nheads_q * (size_t)p->seqlen_q;
+  k.ws_o = static_cast<float*>(workspace);
+  k.ws_lse = k.ws_o + rows * (size_t)S * (size_t)p->headdim;
+  k.q_sb = p->q_strides[0]; k.q_sn = p->q_strides[1]; k.q_sh = p->q_strides[2];
+  k.kc_sb = p->k_strides[0]; k.kc_sn = p->k_strides[1]; k.kc_sh = p->k_strides[2];
+  k.vc_sb = p->v_strides[0]; k.vc_sn = p->v_strides[1]; k.vc_sh = p->v_strides[2];
+  k.kn_sb = params->knew_strides[0]; k.kn_sn = params->knew_strides[1]; k.kn_sh = params->knew_strides[2];
+  k.vn_sb = params->vnew_strides[0]; k.vn_sn = params->vnew_strides[1]; k.vn_sh = params->vnew_strides[2];
+  k.o_sb = p->o_strides[0]; k.o_sn = p->o_strides[1]; k.o_sh = p->o_strides[2];
+  k.B = (int32_t)p->batch; k.Nq = (int32_t)p->seqlen_q; k.cap = (int32_t)p->seqlen_k;
+  k.Hq = (int32_t)p->nheads_q; k.Hkv = (int32_t)p->nheads_kv; k.G = (int32_t)G; k.D = (int32_t)p->headdim;
+  k.dtype = p->dtype == FA_F16 ? fa::kF16 : fa::kBF16;
+  k.scale = p->scale;
+  k.scale_log2 = p->scale * fa::kLog2e;
+  k.causal = p->causal; k.wl = p->window_left; k.wr = p->window_right;
+  k.append = k_new != nullptr;
+  k.S = (int32_t)S;
+  k.n_rb = (int32_t)n_rb;
+  const hipError_t e = fa::launch_kvcache(k, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kv-cache launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
 }
 
 const char* fa_status_string(fa_status status) {

@@ -23,6 +23,9 @@ hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t stream, int stages);
 // Forward and backward, fp32 with D <= 128 (D % 4 == 0): vector-ALU kernels.
 hipError_t launch_fwd_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_bwd_f32(const AttnArgs& a, hipStream_t stream, int stages);
+// Attention against a KV cache (append, split key range, merge); fp16/bf16,
+// D in {64, 128}.
+hipError_t launch_kvcache(const KvArgs& k, hipStream_t stream);
 // D_i = sum_c dout[i,c] * o[i,c] for every query row, any dtype.
 hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream);
 

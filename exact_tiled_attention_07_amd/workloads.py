@@ -10,6 +10,10 @@ FlashAttention 的三步走"), fp16/bf16 with head dimension 64 or 128, hidden s
 2048 and sequence lengths from 512 to 16k ([P4] section "实测数据"), and the
 (2, 32, 8192, 128) timing shape of [P5] "AI模型推理优化Flash Attention原理",
 section "进阶一点的用法".
+
+Decode workloads follow [P4] section "增量解码场景flash_attn_with_kvcache": a
+few new queries per batch entry against a long KV cache whose valid length
+(cache_seqlens) differs between entries, at low batch and long context.
 """
 
 from dataclasses import dataclass, field
@@ -91,3 +95,64 @@ def random_qkv(shape_q, shape_kv, dtype, seed, sigma=1.0):
     v = (torch.randn(shape_kv, generator=g, dtype=torch.float32) * sigma).to(dt)
     do = torch.randn(shape_q, generator=g, dtype=torch.float32).to(dt)
     return q, k, v, do
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Queries against a KV cache: Nq new rows per batch entry, appended first.
+
+    The valid cache lengths before the append are drawn uniformly from
+    [min_len, max_len] (a ragged length mix); cache rows past them hold random
+    values that the result must not depend on."""
+    name: str
+    dtype: str
+    batch: int
+    nq: int
+    nheads_q: int
+    nheads_kv: int
+    headdim: int
+    capacity: int
+    min_len: int
+    max_len: int
+    causal: bool = True
+    window: tuple = (-1, -1)
+    seed: int = 0
+    notes: str = field(default="", compare=False)
+
+
+DECODE_WORKLOADS = {
+    "bf16_decode_b8_hq32_hkv8_d128_cap16384": DecodeWorkload(
+        "bf16_decode_b8_hq32_hkv8_d128_cap16384", "bf16", 8, 1, 32, 8, 128, 16384, 8192, 16383, seed=2001,
+        notes="one new token per entry, GQA 4, long ragged context"),
+    "fp16_decode_b4_hq16_hkv16_d64_cap4096_nq4": DecodeWorkload(
+        "fp16_decode_b4_hq16_hkv16_d64_cap4096_nq4", "fp16", 4, 4, 16, 16, 64, 4096, 1, 4092, seed=2002,
+        notes="four new tokens per entry (multi-token decode), MHA"),
+    "bf16_chunk_b2_hq32_hkv8_d128_cap8192_nq64": DecodeWorkload(
+        "bf16_chunk_b2_hq32_hkv8_d128_cap8192_nq64", "bf16", 2, 64, 32, 8, 128, 8192, 0, 8128, seed=2003,
+        notes="chunked prefill: 64 new tokens against the cache"),
+}
+
+# The decode workload the benchmark times beside the training step.
+BENCH_DECODE_WORKLOAD = "bf16_decode_b8_hq32_hkv8_d128_cap16384"
+
+
+def make_decode_inputs(w: DecodeWorkload, seed=None, batch=None, capacity=None):
+    """Draw q, k_cache, v_cache, k_new, v_new (float32 N(0, 1) rounded to the
+    workload dtype) and cache_seqlens (int32, uniform in [min_len, max_len]
+    clipped to capacity - nq) from one seeded CPU generator, in that order.
+    ``batch`` / ``capacity`` override the shape (same recipe, smaller case; the
+    length bounds scale with the capacity)."""
+    g = torch.Generator("cpu").manual_seed(w.seed if seed is None else seed)
+    b = w.batch if batch is None else batch
+    cap = w.capacity if capacity is None else capacity
+    dt = DTYPES[w.dtype]
+    q = torch.randn((b, w.nq, w.nheads_q, w.headdim), generator=g, dtype=torch.float32).to(dt)
+    kc = torch.randn((b, cap, w.nheads_kv, w.headdim), generator=g, dtype=torch.float32).to(dt)
+    vc = torch.randn((b, cap, w.nheads_kv, w.headdim), generator=g, dtype=torch.float32).to(dt)
+    kn = torch.randn((b, w.nq, w.nheads_kv, w.headdim), generator=g, dtype=torch.float32).to(dt)
+    vn = torch.randn((b, w.nq, w.nheads_kv, w.headdim), generator=g, dtype=torch.float32).to(dt)
+    lo_w, hi_w = w.min_len * cap // w.capacity, w.max_len * cap // w.capacity
+    hi = max(0, min(hi_w, cap - w.nq))
+    lo = min(lo_w, hi)
+    lens = torch.randint(lo, hi + 1, (b,), generator=g, dtype=torch.int64).to(torch.int32)
+    return q, kc, vc, kn, vn, lens

@@ -163,6 +163,57 @@ fa_status fa_bwd_stage(const fa_params* params, int stage, const void* dout, con
                        const void* k, const void* v, const void* o, const float* lse, void* dq,
                        void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Attention against a KV cache (incremental decoding, [P4] section
+ * "增量解码场景flash_attn_with_kvcache": new keys and values are appended to
+ * the cache in place, cache_seqlens gives each batch entry's valid length,
+ * and the key range is split so that few queries against a long cache still
+ * fill the GPU).
+ *
+ * base: batch; seqlen_q = Nq new queries per batch entry; seqlen_k = cache
+ *   capacity in rows; nheads_q, nheads_kv, headdim (64 or 128); q_strides and
+ *   o_strides for q and o (batch, Nq, nheads_q, headdim); k_strides and
+ *   v_strides for the caches (batch, capacity, nheads_kv, headdim); dtype
+ *   FA_F16 or FA_BF16; scale; causal and window as in fa_fwd.
+ * knew_strides, vnew_strides: strides of k_new and v_new (batch, Nq,
+ *   nheads_kv, headdim); ignored when k_new is NULL.
+ * num_splits: parts of the key range per (batch, K/V head), >= 1, or 0 to
+ *   let the library choose enough parts to fill the GPU.
+ */
+typedef struct {
+  fa_params base;
+  int64_t knew_strides[3], vnew_strides[3];
+  int32_t num_splits;
+  int32_t reserved; /* 0 */
+} fa_kvcache_params;
+
+/* Bytes of workspace fa_fwd_kvcache needs: float32 partial outputs and LSEs
+ * of every part, B * nheads_q * Nq * parts * (headdim + 1) floats, rounded
+ * up to 256 bytes. */
+fa_status fa_fwd_kvcache_workspace_size(const fa_kvcache_params* params, size_t* bytes);
+
+/*
+ * For each batch entry b with L = cache_seqlens[b] (clamped to [0, capacity]):
+ *   if k_new is given, rows L .. L+Nq-1 of k_cache / v_cache are overwritten
+ *   with k_new[b] / v_new[b] (rows past the capacity are dropped) and the
+ *   queries see Lk = min(L + Nq, capacity) keys; otherwise Lk = L;
+ *   o[b] = softmax(scale * q[b] K^T + mask) V over cache rows [0, Lk), with
+ *   query i aligned to key i + Lk - Nq and the causal/window rule of fa_fwd;
+ *   lse[b] is its float32 natural-log LSE (B, nheads_q, Nq).
+ *   q [in] (batch, Nq, nheads_q, headdim), dtype
+ *   k_cache, v_cache [in/out] (batch, capacity, nheads_kv, headdim), dtype
+ *   cache_seqlens [in] int32 device array (batch); lengths are read on the
+ *            device, so values outside [0, capacity] are clamped, not rejected
+ *   k_new, v_new [in] both NULL (no append) or both given
+ *   o [out] like q; lse [out] float32 (batch, nheads_q, Nq)
+ *   workspace [scratch] fa_fwd_kvcache_workspace_size bytes, caller-owned
+ * Rows with no visible key get o = 0 and lse = -inf.  fp32 and head sizes
+ * other than 64/128 return FA_ERR_UNSUPPORTED.  Asynchronous on stream.
+ */
+fa_status fa_fwd_kvcache(const fa_kvcache_params* params, const void* q, void* k_cache, void* v_cache,
+                         const int32_t* cache_seqlens, const void* k_new, const void* v_new, void* o,
+                         float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static string naming a status code. */
 const char* fa_status_string(fa_status status);
 

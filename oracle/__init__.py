@@ -14,6 +14,9 @@ Sources (the web pages this method is taken from, cited by title and section):
   section "进阶参数如何配置causal、window_size 与 MQA/GQA" (window_size
   (left, right) with -1 meaning unbounded; fewer K/V heads than Q heads, the Q head
   count an integer multiple of the K/V head count).
+* [P4] same page, section "增量解码场景flash_attn_with_kvcache" (new keys and
+  values appended to a cache in place, cache_seqlens as each batch entry's valid
+  length) -- ``kvcache.py``.
 * [P5] "AI模型推理优化Flash Attention原理" (52runoob.com) -- section "先搞清楚原理"
   (the standard_attention listing: scores scaled by one over the square root of
   the head dimension, softmax over the key axis, product with V).
@@ -26,8 +29,8 @@ differences, a hand-derived golden example and a float64 library cross-check);
 no function here is "parity unpinned".
 """
 
+from .attention import ALL_FUNCTIONS as _ATTENTION_FUNCTIONS
 from .attention import (  # noqa: F401
-    ALL_FUNCTIONS,
     attention_bwd,
     attention_fwd,
     attention_fwd_rows,
@@ -36,3 +39,7 @@ from .attention import (  # noqa: F401
     scores,
     visible,
 )
+from .kvcache import ALL_FUNCTIONS as _KVCACHE_FUNCTIONS
+from .kvcache import kvcache_fwd  # noqa: F401
+
+ALL_FUNCTIONS = _ATTENTION_FUNCTIONS + _KVCACHE_FUNCTIONS

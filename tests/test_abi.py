@@ -34,8 +34,8 @@ def header_functions():
 
 def test_header_declares_expected_entry_points():
     assert header_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_status_string", "fa_last_error",
-         "fa_version"])
+        ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd_kvcache",
+         "fa_fwd_kvcache_workspace_size", "fa_status_string", "fa_last_error", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -47,20 +47,21 @@ def test_library_exports_every_declared_symbol(lib):
         assert name in N.SIGNATURES
 
 
-def test_struct_layout_matches_c(tmp_path):
-    fields = [f for f, _ in N.FaParams._fields_]
+@pytest.mark.parametrize("cname,ctype", [("fa_params", N.FaParams), ("fa_kvcache_params", N.FaKvParams)])
+def test_struct_layout_matches_c(tmp_path, cname, ctype):
+    fields = [f for f, _ in ctype._fields_]
     src = ["#include <stdio.h>", "#include <stddef.h>", '#include "fa.h"', "int main(void){",
-           'printf("%zu\\n", sizeof(fa_params));']
-    src += [f'printf("%zu\\n", offsetof(fa_params, {f}));' for f in fields]
+           f'printf("%zu\\n", sizeof({cname}));']
+    src += [f'printf("%zu\\n", offsetof({cname}, {f}));' for f in fields]
     src += ["return 0;}"]
     c = tmp_path / "layout.c"
     c.write_text("\n".join(src))
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)], check=True)
     vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
-    assert vals[0] == ctypes.sizeof(N.FaParams)
+    assert vals[0] == ctypes.sizeof(ctype)
     for f, off in zip(fields, vals[1:]):
-        assert getattr(N.FaParams, f).offset == off, f
+        assert getattr(ctype, f).offset == off, f
 
 
 def test_header_compiles_as_c_and_cpp(tmp_path):
@@ -260,3 +261,114 @@ def test_library_has_no_undefined_kernel_symbols(lib):
     out = subprocess.run(["nm", "-D", "--undefined-only", N.LIB_PATH], capture_output=True, text=True).stdout
     missing = [l for l in out.splitlines() if "_ZN2fa" in l]
     assert not missing, missing
+
+
+# --------------------------------------------------------------------------
+# fa_fwd_kvcache: host-side validation, workspace size, part count.
+# --------------------------------------------------------------------------
+KQ, KK, KV_, KN, VN, KO, KL, KS, KW = (0x100000 * (i + 1) for i in range(9))
+
+
+def kv_params(num_splits=0, **kw):
+    """B=2, Nq=1, Hq=4, Hkv=2, d=64, capacity 256, contiguous caches."""
+    base = dict(seqlen_q=1, seqlen_k=256, q_strides=(1 * 4 * 64, 4 * 64, 64), o_strides=(1 * 4 * 64, 4 * 64, 64),
+                k_strides=(256 * 2 * 64, 2 * 64, 64), v_strides=(256 * 2 * 64, 2 * 64, 64))
+    base.update({k: v for k, v in kw.items() if not k.startswith(("knew", "vnew", "reserved"))})
+    p = N.FaKvParams()
+    p.base = params(**base)
+    p.knew_strides = N._I64x3(*kw.get("knew_strides", (1 * 2 * 64, 2 * 64, 64)))
+    p.vnew_strides = N._I64x3(*kw.get("vnew_strides", (1 * 2 * 64, 2 * 64, 64)))
+    p.num_splits = num_splits
+    p.reserved = kw.get("reserved", 0)
+    return p
+
+
+def kv_ws(lib, p):
+    n = ctypes.c_size_t()
+    st = lib.fa_fwd_kvcache_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+def call_kv(lib, p, q=KQ, kc=KK, vc=KV_, lens=KS, kn=KN, vn=VN, o=KO, lse=KL, ws=KW, ws_bytes=1 << 30):
+    pp = ctypes.byref(p) if p is not None else None
+    return lib.fa_fwd_kvcache(pp, q, kc, vc, lens, kn, vn, o, lse, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("name,kw", INVALID, ids=[x[0] for x in INVALID])
+def test_kvcache_invalid_arguments(lib, name, kw):
+    assert call_kv(lib, kv_params(**kw)) == N.FA_ERR_INVALID_ARG
+    assert kv_ws(lib, kv_params(**kw))[0] == N.FA_ERR_INVALID_ARG
+
+
+def test_kvcache_specific_validation(lib):
+    assert call_kv(lib, None) == N.FA_ERR_INVALID_ARG
+    assert call_kv(lib, kv_params(num_splits=-1)) == N.FA_ERR_INVALID_ARG
+    assert b"num_splits" in lib.fa_last_error()
+    assert call_kv(lib, kv_params(reserved=1)) == N.FA_ERR_INVALID_ARG
+    assert call_kv(lib, kv_params(), kn=None) == N.FA_ERR_INVALID_ARG       # one of the pair
+    assert b"k_new" in lib.fa_last_error()
+    assert call_kv(lib, kv_params(), lens=None) == N.FA_ERR_INVALID_ARG
+    assert call_kv(lib, kv_params(), lens=KS + 2) == N.FA_ERR_UNSUPPORTED   # int32 array misaligned
+    assert call_kv(lib, kv_params(), q=None) == N.FA_ERR_INVALID_ARG
+    assert call_kv(lib, kv_params(), kc=KK + 8) == N.FA_ERR_UNSUPPORTED
+    assert call_kv(lib, kv_params(), o=KQ) == N.FA_ERR_INVALID_ARG          # o aliases q
+    assert call_kv(lib, kv_params(), lse=KN) == N.FA_ERR_INVALID_ARG        # lse aliases k_new
+    assert call_kv(lib, kv_params(), ws=None) == N.FA_ERR_INVALID_ARG
+    st, need = kv_ws(lib, kv_params())
+    assert st == N.FA_OK
+    assert call_kv(lib, kv_params(), ws_bytes=need - 4) == N.FA_ERR_INVALID_ARG
+    assert b"workspace" in lib.fa_last_error()
+    assert lib.fa_fwd_kvcache_workspace_size(ctypes.byref(kv_params()), None) == N.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("fp32", dict(dtype=0)),
+    ("headdim 96", dict(headdim=96, q_strides=(4 * 96, 4 * 96, 96), o_strides=(4 * 96, 4 * 96, 96),
+                        k_strides=(256 * 2 * 96, 2 * 96, 96), v_strides=(256 * 2 * 96, 2 * 96, 96),
+                        knew_strides=(2 * 96, 2 * 96, 96), vnew_strides=(2 * 96, 2 * 96, 96))),
+    ("new-row stride not 16 bytes", dict(knew_strides=(2 * 64, 2 * 64, 60))),
+    ("negative new-row stride", dict(vnew_strides=(-128, 128, 64))),
+])
+def test_kvcache_unsupported_arguments(lib, name, kw):
+    assert call_kv(lib, kv_params(**kw)) == N.FA_ERR_UNSUPPORTED
+
+
+def test_kvcache_workspace_size_and_parts(lib):
+    # B * Hq * Nq rows, each with parts * (d + 1) floats; parts = num_splits
+    # when given (capped by the 32-key tiles of the capacity).
+    for splits, parts in ((1, 1), (3, 3), (8, 8), (100, 8)):
+        st, n = kv_ws(lib, kv_params(num_splits=splits))
+        assert st == N.FA_OK
+        assert n == ((2 * 4 * 1 * parts * 65 * 4 + 255) // 256) * 256, (splits, n)
+    # num_splits = 0: the library's choice, at least one part and at most a
+    # part per four key tiles (256 keys: 8 tiles -> 2 parts).
+    st, n = kv_ws(lib, kv_params())
+    assert st == N.FA_OK and n == ((2 * 4 * 2 * 65 * 4 + 255) // 256) * 256
+    # Longer caches get more parts when the batch is small.
+    st, n_long = kv_ws(lib, kv_params(seqlen_k=65536, k_strides=(65536 * 128, 128, 64),
+                                      v_strides=(65536 * 128, 128, 64)))
+    assert st == N.FA_OK and n_long > n
+
+
+def test_kvcache_empty_problems_return_ok_without_device(lib):
+    assert call_kv(lib, kv_params(batch=0), q=None, kc=None, vc=None, lens=None, kn=None, vn=None, o=None,
+                   lse=None, ws=None, ws_bytes=0) == N.FA_OK
+    assert call_kv(lib, kv_params(seqlen_q=0), q=None, kc=None, vc=None, lens=None, kn=None, vn=None, o=None,
+                   lse=None, ws=None, ws_bytes=0) == N.FA_OK
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-GPU error path")
+def test_kvcache_valid_call_without_gpu_reports_hip_error(lib):
+    assert call_kv(lib, kv_params()) == N.FA_ERR_HIP
+    assert call_kv(lib, kv_params(), kn=None, vn=None) == N.FA_ERR_HIP
+    # An empty cache with no append needs no cache pointers.
+    p = kv_params(seqlen_k=0)
+    assert call_kv(lib, p, kc=None, vc=None, kn=None, vn=None) == N.FA_ERR_HIP
+
+
+def test_python_kvcache_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 2, 64, dtype=torch.bfloat16)
+    c = torch.zeros(1, 32, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.fwd_kvcache(q, c, c, torch.zeros(1, dtype=torch.int32))
