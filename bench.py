@@ -7,6 +7,11 @@ already resident in HBM.  Prints ONE JSON line (see --help).
 
 Algorithmic FLOP: forward 4*B*Hq*N^2*d halved for causal, backward 2.5x the
 forward (five products per visible score pair instead of two).
+
+Beside the step, the same line carries a "decode" object: fa_fwd_kvcache
+(in-place append + attention against a ragged KV cache) on the bf16 decode
+workload B=8, one new token, Hq=32, Hkv=8, d=128, capacity 16384, timed per
+call with events and priced against HBM bandwidth (it reads the cache once).
 """
 
 import argparse
@@ -33,6 +38,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (whole heads are added until it is reached)")
+    ap.add_argument("--decode-calls", type=int, default=200, help="timed fa_fwd_kvcache calls (0: skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="instead of the benchmark, run a plain device copy of 512 MiB (read 512 MiB, "
                          "write 512 MiB) 5 times: the known-size reference for HBM byte counters")
@@ -180,6 +186,66 @@ def cpu_baseline(w, q, k, v, do, budget_s):
     }
 
 
+def decode_bytes(w, lens):
+    """Algorithmic HBM bytes of one fa_fwd_kvcache call: every visible cache
+    row and new row read once (K and V), the new rows written into the cache,
+    q read, o / lse written, the lengths read."""
+    e = 2
+    lk = [min(max(int(x), 0) + w.nq, w.capacity) for x in lens]
+    kv_read = sum(lk) * w.nheads_kv * w.headdim * e * 2
+    appended = sum(min(w.nq, w.capacity - min(max(int(x), 0), w.capacity)) for x in lens)
+    kv_write = appended * w.nheads_kv * w.headdim * e * 2
+    qo = 2 * w.batch * w.nq * w.nheads_q * w.headdim * e
+    return kv_read + kv_write + qo + w.batch * w.nheads_q * w.nq * 4 + w.batch * 4
+
+
+def decode_leg(calls):
+    """Times fa_fwd_kvcache on the benchmark's decode workload."""
+    import torch
+
+    import exact_tiled_attention_07_amd as fa
+    from exact_tiled_attention_07_amd.workloads import BENCH_DECODE_WORKLOAD, DECODE_WORKLOADS, make_decode_inputs
+
+    w = DECODE_WORKLOADS[BENCH_DECODE_WORKLOAD]
+    dev = torch.device("cuda:0")
+    q, kc, vc, kn, vn, lens = (t.to(dev) for t in make_decode_inputs(w))
+    kw = dict(causal=w.causal, window_size=w.window)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.nheads_q, w.nq), dtype=torch.float32, device=dev)
+    params = fa.make_kv_params(q, kc, vc, out, kn, vn, **kw)
+    ws = torch.empty(fa.kvcache_workspace_size(params), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        # The lengths stay fixed, so every call appends the same rows again and
+        # attends to the same keys: identical work per call.
+        fa.fwd_kvcache(q, kc, vc, lens, kn, vn, out=out, lse=lse, workspace=ws, **kw)
+
+    for _ in range(10):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(calls):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / calls
+    nbytes = decode_bytes(w, lens.tolist())
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {
+        "workload": w.name, "entry_point": "fa_fwd_kvcache",
+        "config": {"batch": w.batch, "new_tokens": w.nq, "nheads_q": w.nheads_q, "nheads_kv": w.nheads_kv,
+                   "headdim": w.headdim, "capacity": w.capacity, "cache_seqlens": lens.tolist(),
+                   "cache_layout": w.kv_layout, "causal": w.causal, "num_splits": "auto"},
+        "calls": calls, "us_per_call": round(us, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
+                     "timed": "whole call (split + merge kernels), events on the launch stream"},
+    }
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -285,6 +351,8 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if args.decode_calls > 0:
+        out["decode"] = decode_leg(args.decode_calls)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q_c, k_c, v_c, do_c, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -70,8 +70,10 @@ struct KvArgs {
   int32_t B, Nq, cap, Hq, Hkv, G, D, dtype;
   float scale, scale_log2;
   int32_t causal, wl, wr, append;
-  int32_t S;     // key-range parts per (batch, kv head, row block)
-  int32_t n_rb;  // blocks of 32 packed query rows (G * Nq rows)
+  int32_t S;          // key-range parts per (batch, kv head, row block)
+  int32_t n_rb;       // blocks of 32 packed query rows (G * Nq rows)
+  int32_t n_split;    // waves of the split phase: B * Hkv * n_rb * S
+  int32_t n_append;   // waves that copy the new rows into the cache
 };
 
 static constexpr float kLog2e = 1.4426950408889634f;

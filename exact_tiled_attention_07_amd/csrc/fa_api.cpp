@@ -190,13 +190,16 @@ int64_t kv_parts(const fa_kvcache_params* kp) {
   const int64_t G = p->nheads_q / p->nheads_kv;
   const int64_t n_rb = (G * p->seqlen_q + 31) / 32;
   const int64_t tiles = std::max<int64_t>(1, (p->seqlen_k + 31) / 32);
-  if (kp->num_splits > 0) return std::min<int64_t>({(int64_t)kp->num_splits, tiles, kMaxKvParts});
-  // Enough single-wave parts for about two waves per SIMD of a 256-CU GPU,
-  // with at least 4 key tiles per part.
-  const int64_t units = std::max<int64_t>(1, p->batch * p->nheads_kv * n_rb);
-  int64_t s = (2048 + units - 1) / units;
-  s = std::min<int64_t>(s, std::max<int64_t>(1, tiles / 4));
-  return std::max<int64_t>(1, std::min<int64_t>(s, kMaxKvParts));
+  int64_t s;
+  if (kp->num_splits > 0) {
+    s = kp->num_splits;
+  } else {
+    // About two single-wave parts per SIMD of a 256-CU GPU, with at least 4
+    // key tiles per part over a full cache.
+    const int64_t units = std::max<int64_t>(1, p->batch * p->nheads_kv * n_rb);
+    s = std::min<int64_t>((2048 + units - 1) / units, std::max<int64_t>(1, tiles / 4));
+  }
+  return std::max<int64_t>(1, std::min<int64_t>({s, tiles, kMaxKvParts}));
 }
 
 size_t kv_workspace_bytes(const fa_kvcache_params* kp) {
@@ -353,7 +356,10 @@ fa_status fa_fwd_kvcache(const fa_kvcache_params* params, const void* q, void* k
   const int64_t G = p->nheads_q / p->nheads_kv;
   const int64_t n_rb = (G * p->seqlen_q + 31) / 32;
   const int64_t S = kv_parts(params);
-  if (p->batch * p->nheads_kv * n_rb * S >= (int64_t(1) << 31))
+  const int64_t n_split = p->batch * p->nheads_kv * n_rb * S;
+  const int64_t n_append =
+      k_new ? (2 * p->batch * p->seqlen_q * p->nheads_kv * (p->headdim / 8) + 63) / 64 : 0;
+  if (n_split + n_append >= (int64_t(1) << 31))
     return fail(FA_ERR_UNSUPPORTED, "launch grid would exceed 2^31 workgroups");
   if ((s = check_device()) != FA_OK) return s;
 
@@ -378,6 +384,8 @@ fa_status fa_fwd_kvcache(const fa_kvcache_params* params, const void* q, void* k
   k.append = k_new != nullptr;
   k.S = (int32_t)S;
   k.n_rb = (int32_t)n_rb;
+  k.n_split = (int32_t)n_split;
+  k.n_append = (int32_t)n_append;
   const hipError_t e = fa::launch_kvcache(k, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kv-cache launch failed: %s", hipGetErrorString(e));
   return FA_OK;

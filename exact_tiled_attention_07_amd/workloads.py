@@ -117,13 +117,18 @@ class DecodeWorkload:
     causal: bool = True
     window: tuple = (-1, -1)
     seed: int = 0
+    # Cache storage order: "bshd" stores (batch, capacity, heads, headdim);
+    # "bhsd" stores (batch, heads, capacity, headdim), so the 32 rows of a key
+    # tile of one head are one contiguous 8 KB block (d = 128).  Both are
+    # handed over as (batch, capacity, heads, headdim) views with strides.
+    kv_layout: str = "bshd"
     notes: str = field(default="", compare=False)
 
 
 DECODE_WORKLOADS = {
     "bf16_decode_b8_hq32_hkv8_d128_cap16384": DecodeWorkload(
         "bf16_decode_b8_hq32_hkv8_d128_cap16384", "bf16", 8, 1, 32, 8, 128, 16384, 8192, 16383, seed=2001,
-        notes="one new token per entry, GQA 4, long ragged context"),
+        kv_layout="bhsd", notes="one new token per entry, GQA 4, long ragged context, head-major cache"),
     "fp16_decode_b4_hq16_hkv16_d64_cap4096_nq4": DecodeWorkload(
         "fp16_decode_b4_hq16_hkv16_d64_cap4096_nq4", "fp16", 4, 4, 16, 16, 64, 4096, 1, 4092, seed=2002,
         notes="four new tokens per entry (multi-token decode), MHA"),
@@ -149,6 +154,11 @@ def make_decode_inputs(w: DecodeWorkload, seed=None, batch=None, capacity=None):
     q = torch.randn((b, w.nq, w.nheads_q, w.headdim), generator=g, dtype=torch.float32).to(dt)
     kc = torch.randn((b, cap, w.nheads_kv, w.headdim), generator=g, dtype=torch.float32).to(dt)
     vc = torch.randn((b, cap, w.nheads_kv, w.headdim), generator=g, dtype=torch.float32).to(dt)
+    if w.kv_layout == "bhsd":
+        kc = kc.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        vc = vc.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    elif w.kv_layout != "bshd":
+        raise ValueError(f"unknown cache layout {w.kv_layout}")
     kn = torch.randn((b, w.nq, w.nheads_kv, w.headdim), generator=g, dtype=torch.float32).to(dt)
     vn = torch.randn((b, w.nq, w.nheads_kv, w.headdim), generator=g, dtype=torch.float32).to(dt)
     lo_w, hi_w = w.min_len * cap // w.capacity, w.max_len * cap // w.capacity

@@ -178,7 +178,10 @@ fa_status fa_bwd_stage(const fa_params* params, int stage, const void* dout, con
  * knew_strides, vnew_strides: strides of k_new and v_new (batch, Nq,
  *   nheads_kv, headdim); ignored when k_new is NULL.
  * num_splits: parts of the key range per (batch, K/V head), >= 1, or 0 to
- *   let the library choose enough parts to fill the GPU.
+ *   let the library choose enough parts to fill the GPU; at most the
+ *   capacity's count of 32-key tiles (and 1024) are used.  The visible key
+ *   tiles of each block of queries are cut into that many equal runs.  The
+ *   split only changes rounding, never the result's definition.
  */
 typedef struct {
   fa_params base;
