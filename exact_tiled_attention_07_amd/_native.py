@@ -44,6 +44,14 @@ class FaParams(ctypes.Structure):
     ]
 
 
+class FaVarlenParams(ctypes.Structure):
+    _fields_ = [
+        ("base", FaParams),
+        ("total_q", ctypes.c_int64),
+        ("total_k", ctypes.c_int64),
+    ]
+
+
 class FaKvParams(ctypes.Structure):
     _fields_ = [
         ("base", FaParams),
@@ -56,6 +64,7 @@ class FaKvParams(ctypes.Structure):
 
 _P = ctypes.POINTER(FaParams)
 _PK = ctypes.POINTER(FaKvParams)
+_PV = ctypes.POINTER(FaVarlenParams)
 _V = ctypes.c_void_p
 SIGNATURES = {
     "fa_fwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V]),
@@ -63,6 +72,9 @@ SIGNATURES = {
     "fa_bwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "fa_bwd_stage": (ctypes.c_int, [_P, ctypes.c_int, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t,
                                     _V]),
+    "fa_fwd_varlen": (ctypes.c_int, [_PV, _V, _V, _V, _V, _V, _V, _V, _V]),
+    "fa_bwd_varlen_workspace_size": (ctypes.c_int, [_PV, ctypes.POINTER(ctypes.c_size_t)]),
+    "fa_bwd_varlen": (ctypes.c_int, [_PV, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "fa_fwd_kvcache_workspace_size": (ctypes.c_int, [_PK, ctypes.POINTER(ctypes.c_size_t)]),
     "fa_fwd_kvcache": (ctypes.c_int, [_PK, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -229,6 +241,108 @@ def bwd(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1), scale=No
     return dq, dk, dv
 
 
+def make_varlen_params(q, k, v, o, max_seqlen_q, max_seqlen_k, *, causal=False, window_size=(-1, -1),
+                       scale=None):
+    """FaVarlenParams for packed tensors q/o (total_q, Hq, d), k/v (total_k, Hkv, d)."""
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or o.dim() != 3:
+        raise ValueError("packed q, k, v, o must be 3-D (total, nheads, headdim)")
+    if q.dtype not in _TORCH_DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for t in (k, v, o):
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v (and o) must share one dtype")
+    if k.shape != v.shape or o.shape != q.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("shape mismatch between q, k, v and o")
+    for t in (q, k, v, o):
+        if t.stride(2) != 1 and t.shape[2] > 1:
+            raise ValueError("the headdim axis must be contiguous (stride 1)")
+    wl, wr = window_size
+    p = FaVarlenParams()
+    b = p.base
+    b.batch = 0  # set by the caller (number of sequences)
+    b.seqlen_q, b.seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+    b.nheads_q, b.nheads_kv, b.headdim = q.shape[1], k.shape[1], q.shape[2]
+    b.q_strides = _I64x3(0, q.stride(0), q.stride(1))
+    b.k_strides = _I64x3(0, k.stride(0), k.stride(1))
+    b.v_strides = _I64x3(0, v.stride(0), v.stride(1))
+    b.o_strides = _I64x3(0, o.stride(0), o.stride(1))
+    b.dtype = _TORCH_DTYPE[q.dtype]
+    b.scale = (1.0 / math.sqrt(q.shape[2])) if scale is None else float(scale)
+    b.causal = 1 if causal else 0
+    b.window_left, b.window_right = int(wl), int(wr)
+    p.total_q, p.total_k = q.shape[0], k.shape[0]
+    return p
+
+
+def _check_offsets(cu, name):
+    if cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous() or cu.numel() < 1:
+        raise ValueError(f"{name} must be a contiguous 1-D int32 tensor of batch + 1 offsets")
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,
+               window_size=(-1, -1), scale=None, out=None, lse=None):
+    """Forward over a packed batch: returns (o, lse).
+
+    q (total_q, Hq, d); k, v (total_k, Hkv, d); cu_seqlens_* int32 (batch + 1,)
+    on the device; max_seqlen_* bound the sequence lengths.  o like q; lse
+    float32 (Hq, total_q).
+    """
+    _require_gpu(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    _check_offsets(cu_seqlens_q, "cu_seqlens_q")
+    _check_offsets(cu_seqlens_k, "cu_seqlens_k")
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    p = make_varlen_params(q, k, v, out, max_seqlen_q, max_seqlen_k, causal=causal, window_size=window_size,
+                           scale=scale)
+    p.base.batch = cu_seqlens_q.numel() - 1
+    with torch.cuda.device(q.device):
+        _check(lib.fa_fwd_varlen(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                                 _ptr(cu_seqlens_k), _ptr(out), _ptr(lse), _stream(q.device)))
+    return out, lse
+
+
+def bwd_varlen_workspace_size(params):
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.fa_bwd_varlen_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return n.value
+
+
+def bwd_varlen(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *,
+               causal=False, window_size=(-1, -1), scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward over a packed batch: returns (dq, dk, dv) of L = sum(out * dout)."""
+    _require_gpu(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k)
+    _check_offsets(cu_seqlens_q, "cu_seqlens_q")
+    _check_offsets(cu_seqlens_k, "cu_seqlens_k")
+    lib = load_library()
+    if dout.shape != q.shape or dout.dtype != q.dtype or dout.stride() != out.stride():
+        raise ValueError("dout must have the shape, dtype and strides of out")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0]) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (nheads_q, total_q) tensor")
+    p = make_varlen_params(q, k, v, out, max_seqlen_q, max_seqlen_k, causal=causal, window_size=window_size,
+                           scale=scale)
+    p.base.batch = cu_seqlens_q.numel() - 1
+    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device) if dv is None else dv
+    for g, ref in ((dq, q), (dk, k), (dv, v)):
+        if g.shape != ref.shape or g.stride() != ref.stride() or g.dtype != ref.dtype:
+            raise ValueError("gradient buffers must match the shape, strides and dtype of q/k/v")
+    need = bwd_varlen_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd_varlen(ctypes.byref(p), _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                 _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return dq, dk, dv
+
+
 def make_kv_params(q, k_cache, v_cache, out, k_new=None, v_new=None, *, causal=False, window_size=(-1, -1),
                    scale=None, num_splits=0):
     """FaKvParams: q/out (B, Nq, Hq, d), caches (B, capacity, Hkv, d), new rows like q with Hkv heads."""
@@ -312,3 +426,70 @@ class _Attention(torch.autograd.Function):
 def attention(q, k, v, *, causal=False, window_size=(-1, -1), scale=None):
     """Differentiable exact attention over (batch, seqlen, nheads, headdim) tensors."""
     return _Attention.apply(q, k, v, causal, tuple(window_size), scale)
+
+
+class _AttentionVarlen(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_q, cu_k, max_q, max_k, causal, window_size, scale):
+        o, lse = fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k, causal=causal, window_size=window_size, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse, cu_q, cu_k)
+        ctx.cfg = (max_q, max_k, causal, window_size, scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, cu_q, cu_k = ctx.saved_tensors
+        max_q, max_k, causal, window_size, scale = ctx.cfg
+        if do.stride() != o.stride():
+            do = torch.empty_strided(o.shape, o.stride(), dtype=o.dtype, device=o.device).copy_(do)
+        dq, dk, dv = bwd_varlen(do, q, k, v, o, lse, cu_q, cu_k, max_q, max_k, causal=causal,
+                                window_size=window_size, scale=scale)
+        return dq, dk, dv, None, None, None, None, None, None, None
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,
+                     window_size=(-1, -1), scale=None):
+    """Differentiable exact attention over a packed variable-length batch."""
+    return _AttentionVarlen.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, int(max_seqlen_q), int(max_seqlen_k),
+                                  causal, tuple(window_size), scale)
+
+
+def _unpack_qkv(qkv):
+    if qkv.dim() != 5 or qkv.shape[2] != 3:
+        raise ValueError("qkv must be (batch, seqlen, 3, nheads, headdim)")
+    return qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+
+
+class _AttentionQkvPacked(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, qkv, causal, window_size, scale):
+        q, k, v = _unpack_qkv(qkv)
+        o, lse = fwd(q, k, v, causal=causal, window_size=window_size, scale=scale)
+        ctx.save_for_backward(qkv, o, lse)
+        ctx.cfg = (causal, window_size, scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        qkv, o, lse = ctx.saved_tensors
+        causal, window_size, scale = ctx.cfg
+        q, k, v = _unpack_qkv(qkv)
+        if do.stride() != o.stride():
+            do = torch.empty_strided(o.shape, o.stride(), dtype=o.dtype, device=o.device).copy_(do)
+        # The gradient is written straight into one packed tensor through
+        # views with the strides of q, k and v.
+        dqkv = torch.empty_like(qkv)
+        dq, dk, dv = _unpack_qkv(dqkv)
+        bwd(do, q, k, v, o, lse, causal=causal, window_size=window_size, scale=scale, dq=dq, dk=dk, dv=dv)
+        return dqkv, None, None, None
+
+
+def fwd_qkvpacked(qkv, *, causal=False, window_size=(-1, -1), scale=None, out=None, lse=None):
+    """Forward of packed (batch, seqlen, 3, nheads, headdim) q/k/v: returns (o, lse)."""
+    q, k, v = _unpack_qkv(qkv)
+    return fwd(q, k, v, causal=causal, window_size=window_size, scale=scale, out=out, lse=lse)
+
+
+def attention_qkvpacked(qkv, *, causal=False, window_size=(-1, -1), scale=None):
+    """Differentiable attention over packed q/k/v; the gradient is packed the same way."""
+    return _AttentionQkvPacked.apply(qkv, causal, tuple(window_size), scale)

@@ -10,14 +10,10 @@
 //
 // Three kernels, none with atomics (results are bitwise repeatable):
 //   preprocess  D_i for every query row (fp32 workspace)
-//   dK/dV       one workgroup per (batch, kv head, tile of 32*NW keys); each
-//               wave keeps its 32 keys' K and V in registers and its dK^T, dV^T
-//               accumulators in registers, loops over the query heads of the
-//               group and the visible query tiles (one pipelined loop):
-//                 S  = Q K^T        (A = Q row chunks in LDS, B = K registers)
-//                 dP = dO V^T       (A = dO row chunks in LDS, B = V registers)
-//                 dV^T += dO^T P    (A = dO read transposed from LDS, B = P)
-//                 dK^T += Q^T dS    (A = Q read transposed from LDS, B = dS)
+//   dK/dV       one workgroup per (batch, kv head, tile of 128 keys) with
+//               score waves and gradient waves (described at the kernel):
+//                 S  = Q K^T,  dP = dO V^T       (score waves)
+//                 dV^T += dO^T P,  dK^T += Q^T dS (gradient waves, one item later)
 //               GQA sums over the group inside the workgroup.
 //   dQ          one workgroup per (batch, query head, tile of 32*NW queries);
 //               the forward's layout (one query per lane):
@@ -46,7 +42,7 @@ namespace fa {
 template <int ELT>  // element bytes: 4 (fp32) or 2 (fp16/bf16)
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a) {
   constexpr int EPC = 16 / ELT;  // elements per 16-byte chunk
-  const int nq_pad = (a.Nq + 127) / 128 * 128;
+  const int nq_pad = (a.Nq + 127) / 128 * 128;  // of the longest sequence for packed batches
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   const int64_t rows = (int64_t)a.B * nq_pad * a.Hq;
@@ -54,11 +50,14 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a) {
   using Acc = typename std::conditional<ELT == 4, double, float>::type;
   Acc acc = 0;
   int h = 0, i = 0, b = 0;
+  bool active = false;  // row inside its sequence's padded range
   if (row < rows) {
     h = (int)(row % a.Hq);
     const int64_t t = row / a.Hq;
     i = (int)(t % nq_pad);
     b = (int)(t / nq_pad);
+    bind_seq(a, b);
+    active = i < (a.Nq + 127) / 128 * 128;
     if (i < a.Nq) {
       const int64_t base = (b * a.o_sb + (int64_t)i * a.o_sn + h * a.o_sh) * ELT;
       const char* dop = static_cast<const char*>(a.dout) + base;
@@ -83,12 +82,12 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-  if (row < rows && sub == 0) {
-    const int64_t o = ((int64_t)b * a.Hq + h) * nq_pad + i;
+  if (active && sub == 0) {
+    const int64_t o = b * a.ws_sb + h * a.ws_sh + i;
     a.dsum[o] = (float)acc;
     float l2 = INFINITY;
     if (i < a.Nq) {
-      const float L = a.lse[((int64_t)b * a.Hq + h) * a.Nq + i];
+      const float L = a.lse[b * a.lse_sb + h * a.lse_sh + i];
       if (L != -INFINITY) l2 = L * kLog2e;
     }
     a.lse2[o] = l2;
@@ -110,17 +109,8 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
 #ifndef FA_DKDV_BMQ
 #define FA_DKDV_BMQ 64  // queries per dK/dV iteration
 #endif
-#ifndef FA_DKDV_NW
-#define FA_DKDV_NW 4  // waves per dK/dV workgroup (32 keys each)
-#endif
-#ifndef FA_DKDV_WPE
-#define FA_DKDV_WPE 1
-#endif
 #ifndef FA_DQ_RING
 #define FA_DQ_RING 3  // LDS operands in flight ahead of the MFMA that uses them
-#endif
-#ifndef FA_DKDV_WS
-#define FA_DKDV_WS 1  // dK/dV with specialised score and gradient waves
 #endif
 #ifndef FA_DQ_BN
 #define FA_DQ_BN 64  // keys per dQ iteration
@@ -131,222 +121,6 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
 #ifndef FA_DQ_WPE
 #define FA_DQ_WPE 2
 #endif
-
-// ---------------------------------------------------------------------------
-// dK / dV
-// ---------------------------------------------------------------------------
-template <class T, int D, int BMQ, int NW>
-struct DkdvCtx {
-  static constexpr int TILE = BMQ * D;
-  uint16_t* smem;  // [buf][Q tile, dO tile]
-  float* rstat;    // [buf][lse2[BMQ], dsum[BMQ]]
-  const AttnArgs* a;
-  int b, hk, k0, k_last, key, qt_lo, n_qt, n_items, wave, lane, hf, nq_pad;
-  float c;
-  u32x4 kf[D / 16], vf[D / 16];
-  f32x16 dka[D / 32], dva[D / 32];
-  SwzOffsets<D> off;
-  DmaTile<D, BMQ, NW> qd, dd;
-
-  // Work item w -> (query head of the group, first query row).  Query tiles
-  // run from the last one down, with the heads of the group innermost: the
-  // workgroups of one K/V head that run at the same time then read the same
-  // Q/dO tiles at about the same time, and those come from L2.
-  __device__ __forceinline__ int item_row(int w) const { return (qt_lo + n_qt - 1 - w / a->G) * BMQ; }
-  __device__ __forceinline__ int item_head(int w) const { return hk * a->G + w % a->G; }
-
-  // Start the loads of work item w.
-  template <int BUF>
-  __device__ __forceinline__ void issue(int w) {
-    const int i0 = item_row(w);
-    const int hq = item_head(w);
-    qd.issue(static_cast<const uint16_t*>(a->q) + b * a->q_sb + hq * a->q_sh, a->q_sn, i0, a->Nq,
-             smem + BUF * 2 * TILE, wave);
-    dd.issue(static_cast<const uint16_t*>(a->dout) + b * a->o_sb + hq * a->o_sh, a->o_sn, i0, a->Nq,
-             smem + BUF * 2 * TILE + TILE, wave);
-    if (wave == 0) {
-      const int64_t ro = ((int64_t)b * a->Hq + hq) * nq_pad + i0;
-      if (lane < BMQ / 4) {
-        // 4 floats per lane: lse2 then dsum rows of this tile (padded arrays).
-        dma16(a->lse2 + ro + 4 * lane, reinterpret_cast<uint16_t*>(rstat + BUF * 2 * BMQ));
-      } else if (lane < BMQ / 2) {
-        dma16(a->dsum + ro + 4 * (lane - BMQ / 4), reinterpret_cast<uint16_t*>(rstat + BUF * 2 * BMQ));
-      }
-    }
-  }
-
-  template <int BUF>
-  __device__ __forceinline__ void step(int w) {
-    const char* Qs = reinterpret_cast<const char*>(smem + BUF * 2 * TILE);
-    const char* dOs = Qs + TILE * 2;
-    const float* lse2s = rstat + BUF * 2 * BMQ;
-    const float* dsums = lse2s + BMQ;
-    const int i0 = item_row(w);
-    if (w + 1 < n_items) issue<1 - BUF>(w + 1);
-    const int i_end = min(i0 + BMQ, a->Nq) - 1;
-    const bool full = (key_lo(*a, i_end) <= k0) && (key_hi(*a, i0) >= k_last);
-    step_items(Qs, dOs, lse2s, dsums, i0, full);
-    wait_all_loads();
-    __syncthreads();
-  }
-
-  // P = exp2(s*c - lse2), dS = P * (dP - D) for one 32-query block, packed as
-  // B operands pf[2], dsf[2] (entries r of block qb are query 32*qb + 8*(r/4)
-  // + 4*hf + r%4; l4/d4 hold the row statistics of that order).
-  __device__ __forceinline__ void softmax_grad_elem(const f32x16& sv, const f32x16& dpv, const f32x4 (&l4)[4],
-                                                    const f32x4 (&d4)[4], int r, float (&pb)[8], float (&db_)[8],
-                                                    u32x4* pf, u32x4* dsf) {
-    const float pr = fast_exp2(fmaf(sv[r], c, -l4[r >> 2][r & 3]));
-    pb[r & 7] = pr;
-    db_[r & 7] = pr * (dpv[r] - d4[r >> 2][r & 3]);
-    if ((r & 7) == 7) {
-      pf[r >> 3] = u32x4{T::pack(pb[0], pb[1]), T::pack(pb[2], pb[3]), T::pack(pb[4], pb[5]), T::pack(pb[6], pb[7])};
-      dsf[r >> 3] = u32x4{T::pack(db_[0], db_[1]), T::pack(db_[2], db_[3]), T::pack(db_[4], db_[5]),
-                          T::pack(db_[6], db_[7])};
-    }
-  }
-
-  // The products of one item.  (A hand-pipelined variant that overlaps the
-  // VALU work of one 32-query block with the MFMAs of the other needs more
-  // than the 512 registers a wave can hold here and was slower.)
-  __device__ __forceinline__ void step_items(const char* Qs, const char* dOs, const float* lse2s, const float* dsums,
-                                             int i0, bool full) {
-    // S = Q K^T and dP = dO V^T; [qb][r] is query i0 + 32*qb + 8*(r/4) + 4*hf + r%4.
-    f32x16 s[BMQ / 32], dp[BMQ / 32];
-#pragma unroll
-    for (int qb = 0; qb < BMQ / 32; ++qb) s[qb] = dp[qb] = f32x16{};
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-#pragma unroll
-      for (int qb = 0; qb < BMQ / 32; ++qb) {
-        s[qb] = T::mfma(off.row_chunk(Qs, qb, st), kf[st], s[qb]);
-        dp[qb] = T::mfma(off.row_chunk(dOs, qb, st), vf[st], dp[qb]);
-      }
-    }
-    if (!full) {
-#pragma unroll
-      for (int qb = 0; qb < BMQ / 32; ++qb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = i0 + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key < key_lo(*a, i) || key > key_hi(*a, i)) s[qb][r] = -INFINITY;
-        }
-      }
-    }
-    u32x4 pf[BMQ / 16], dsf[BMQ / 16];
-#pragma unroll
-    for (int qb = 0; qb < BMQ / 32; ++qb) {
-      f32x4 l4[4], d4[4];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        l4[g4] = *reinterpret_cast<const f32x4*>(lse2s + 32 * qb + 8 * g4 + 4 * hf);
-        d4[g4] = *reinterpret_cast<const f32x4*>(dsums + 32 * qb + 8 * g4 + 4 * hf);
-      }
-      float pb[8], dbf[8];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) softmax_grad_elem(s[qb], dp[qb], l4, d4, r, pb, dbf, pf + 2 * qb, dsf + 2 * qb);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS, operands read transposed from the tiles.
-#pragma unroll
-    for (int si = 0; si < BMQ / 16; ++si) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        dva[db] = T::mfma(off.tr_operand(dOs, si, db), pf[si], dva[db]);
-        dka[db] = T::mfma(off.tr_operand(Qs, si, db), dsf[si], dka[db]);
-      }
-    }
-  }
-};
-
-template <class T, int D, int BMQ, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DKDV_WPE, FA_DKDV_WPE))) void bwd_dkdv_kernel(AttnArgs a) {
-  constexpr int BNK = NW * 32;  // keys per workgroup
-  using Ctx = DkdvCtx<T, D, BMQ, NW>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * Ctx::TILE];
-  __shared__ __attribute__((aligned(16))) float rstat[2 * 2 * BMQ];
-  static_assert(2 * 2 * Ctx::TILE * 2 <= 65536, "LDS offsets must fit the 16-bit immediate");
-  static_assert(BMQ <= 128 && 128 % BMQ == 0, "row statistics are padded to 128 rows");
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hf = lane >> 5;
-  const int n_kt = (a.Nk + BNK - 1) / BNK;
-  // Under a causal mask the first key tiles see the most queries: run them first.
-  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_kt, 1, false, a.xcd_remap);
-
-  Ctx x;
-  x.smem = smem;
-  x.rstat = rstat;
-  x.a = &a;
-  x.b = it.unit / a.Hkv;
-  x.hk = it.unit % a.Hkv;
-  x.k0 = it.tile * BNK;
-  x.key = x.k0 + wave * 32 + l32;  // this lane's key (accumulator column)
-  x.wave = wave;
-  x.lane = lane;
-  x.hf = hf;
-  x.c = a.scale_log2;
-  x.nq_pad = (a.Nq + 127) / 128 * 128;
-
-  const uint16_t* Kp = static_cast<const uint16_t*>(a.k) + x.b * a.k_sb + x.hk * a.k_sh;
-  const uint16_t* Vp = static_cast<const uint16_t*>(a.v) + x.b * a.v_sb + x.hk * a.v_sh;
-  // K and V as B operands (lane: key, d = 16*st + 8*hf + 0..7).
-  if (x.key < a.Nk) {
-    const uint16_t* kr = Kp + (int64_t)x.key * a.k_sn + 8 * hf;
-    const uint16_t* vr = Vp + (int64_t)x.key * a.v_sn + 8 * hf;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      x.kf[st] = *reinterpret_cast<const u32x4*>(kr + 16 * st);
-      x.vf[st] = *reinterpret_cast<const u32x4*>(vr + 16 * st);
-    }
-  } else {
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) x.kf[st] = x.vf[st] = u32x4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) x.dka[db] = x.dva[db] = f32x16{};
-
-  x.k_last = min(x.k0 + BNK, a.Nk) - 1;
-  const int i_lo = query_lo(a, x.k0), i_hi = query_hi(a, x.k_last);
-  x.qt_lo = i_lo / BMQ;
-  x.n_qt = (i_hi >= i_lo) ? i_hi / BMQ - x.qt_lo + 1 : 0;
-  x.n_items = x.n_qt * a.G;  // (query head of the group, query tile) pairs
-  x.off.init(lane);
-  x.qd.init(wave, lane, a.q_sn);
-  x.dd.init(wave, lane, a.o_sn);
-
-  if (x.n_items > 0) {
-    x.template issue<0>(0);
-    wait_all_loads();
-  }
-  __syncthreads();
-  int w = 0;
-  for (; w + 1 < x.n_items; w += 2) {
-    x.template step<0>(w);
-    x.template step<1>(w + 1);
-  }
-  if (w < x.n_items) x.template step<0>(w);
-
-  // Store dK = scale * dK and dV: lane holds d rows 32*db + 8*g4 + 4*hf + 0..3.
-  if (x.key < a.Nk) {
-    uint16_t* dkp = static_cast<uint16_t*>(a.dk) + x.b * a.k_sb + x.hk * a.k_sh + (int64_t)x.key * a.k_sn;
-    uint16_t* dvp = static_cast<uint16_t*>(a.dv) + x.b * a.v_sb + x.hk * a.v_sh + (int64_t)x.key * a.v_sn;
-    const float sc = a.scale;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * db + 8 * g4 + 4 * hf;
-        *reinterpret_cast<u32x2*>(dkp + d0) =
-            u32x2{T::pack(x.dka[db][4 * g4] * sc, x.dka[db][4 * g4 + 1] * sc),
-                  T::pack(x.dka[db][4 * g4 + 2] * sc, x.dka[db][4 * g4 + 3] * sc)};
-        *reinterpret_cast<u32x2*>(dvp + d0) =
-            u32x2{T::pack(x.dva[db][4 * g4], x.dva[db][4 * g4 + 1]),
-                  T::pack(x.dva[db][4 * g4 + 2], x.dva[db][4 * g4 + 3])};
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dK / dV with specialised waves.
@@ -390,7 +164,7 @@ struct DkdvWs {
   using L = DkdvWsLayout<D, BMQ>;
   char* smem;  // [slot][Q tile, dO tile], [score wave][P, dS images], [slot][lse2, dsum]
   const AttnArgs* a;
-  int b, hk, k0, k_last, key, qt_lo, n_qt, n_items, wave, kb, lane, hf, nq_pad;
+  int b, hk, k0, k_last, key, qt_lo, n_qt, n_items, wave, kb, lane, hf;
   float c;
   SwzOffsets<D> off;
   // The score waves issue every tile load.  (A wave whose transposing LDS
@@ -427,7 +201,7 @@ struct DkdvWs {
     dd.issue(static_cast<const uint16_t*>(a->dout) + b * a->o_sb + hq * a->o_sh, a->o_sn, i0, a->Nq,
              reinterpret_cast<uint16_t*>(slot_tiles(slot) + L::TILE * 2), kb);
     if (kb == L::KW - 1) {
-      const int64_t ro = ((int64_t)b * a->Hq + hq) * nq_pad + i0;
+      const int64_t ro = b * a->ws_sb + hq * a->ws_sh + i0;
       uint16_t* r = reinterpret_cast<uint16_t*>(slot_stats(slot));
       if (lane < BMQ / 4) {
         dma16(a->lse2 + ro + 4 * lane, r);
@@ -648,13 +422,14 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
   x.b = it.unit / a.Hkv;
   x.hk = it.unit % a.Hkv;
   x.k0 = it.tile * L::BNK;
+  bind_seq(a, x.b);
+  if (x.k0 >= a.Nk) return;  // past the end of a shorter packed sequence (whole workgroup)
   x.wave = wave;
   x.kb = wave % L::KW;
   x.lane = lane;
   x.hf = lane >> 5;
   x.key = x.k0 + x.kb * 32 + (lane & 31);  // this lane's key (accumulator column)
   x.c = a.scale_log2;
-  x.nq_pad = (a.Nq + 127) / 128 * 128;
   x.k_last = min(x.k0 + L::BNK, a.Nk) - 1;
   const int i_lo = query_lo(a, x.k0), i_hi = query_hi(a, x.k_last);
   x.qt_lo = i_lo / BMQ;
@@ -814,6 +589,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
   const int hq = hk * a.G + it.sub;
   const int q0 = it.tile * BM;
   const int qrow = q0 + wave * 32 + l32;
+  bind_seq(a, b);
+  if (q0 >= a.Nq) return;  // past the end of a shorter packed sequence (whole workgroup)
 
   Ctx x;
   x.smem = smem;
@@ -837,7 +614,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
       x.qf[st] = *reinterpret_cast<const u32x4*>(qr + 16 * st);
       x.df[st] = *reinterpret_cast<const u32x4*>(dr + 16 * st);
     }
-    const int64_t ri = ((int64_t)b * a.Hq + hq) * ((a.Nq + 127) / 128 * 128) + qrow;
+    const int64_t ri = b * a.ws_sb + hq * a.ws_sh + qrow;
     x.lse2 = a.lse2[ri];
     x.dsum = a.dsum[ri];
   } else {
@@ -897,7 +674,6 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream, int stages
   }
   AttnArgs args = a;
   args.xcd_remap = a.xcd_remap && ((a.B * a.Hkv) % 8 == 0);
-#if FA_DKDV_WS
   using WL = DkdvWsLayout<D, FA_DKDV_BMQ>;
   const int n_kt = (a.Nk + WL::BNK - 1) / WL::BNK;
   const int64_t grid_kv = (int64_t)a.B * a.Hkv * n_kt;
@@ -907,16 +683,6 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream, int stages
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-#else
-  const int n_kt = (a.Nk + FA_DKDV_NW * 32 - 1) / (FA_DKDV_NW * 32);
-  const int64_t grid_kv = (int64_t)a.B * a.Hkv * n_kt;
-  if (grid_kv > 0 && (stages & kStageDkdv)) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, FA_DKDV_BMQ, FA_DKDV_NW>), dim3((unsigned)grid_kv),
-                       dim3(FA_DKDV_NW * 64), 0, stream, args);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-#endif
   const int n_qt = (a.Nq + FA_DQ_NW * 32 - 1) / (FA_DQ_NW * 32);
   const int64_t grid_q = (int64_t)a.B * a.Hkv * n_qt * a.G;
   if (grid_q > 0 && (stages & kStageDq)) {

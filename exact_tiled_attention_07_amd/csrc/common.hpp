@@ -47,7 +47,53 @@ struct AttnArgs {
   int32_t causal, wl, wr;  // wl/wr: -1 = unbounded
   int32_t delta;     // Nk - Nq (queries aligned to the end of the keys)
   int32_t xcd_remap; // 1: map consecutive workgroup ids onto one XCD's work
+  // Element strides of the float32 row arrays: lse[b*lse_sb + h*lse_sh + i],
+  // dsum / lse2[b*ws_sb + h*ws_sh + i].
+  int64_t lse_sb, lse_sh;
+  int64_t ws_sb, ws_sh;
+  // Packed variable-length batches (NULL: every batch entry has Nq / Nk rows).
+  // Sequence b holds rows cu_q[b] .. cu_q[b+1]-1 of q, o, dout, dq and rows
+  // cu_k[b] .. cu_k[b+1]-1 of k, v, dk, dv; Nq / Nk are then the longest
+  // lengths (they size the grid) and total_q / total_k the packed row counts.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t total_q, total_k;
 };
+
+// Binds the arguments to batch entry b of a packed variable-length batch:
+// every pointer moves to the sequence's first row (the workspace rows to
+// cu_q[b] + 128*b, leaving each sequence its own padding rows), the batch
+// strides become 0 and Nq / Nk / delta become the sequence's own.  Offsets
+// are clamped to the packed tensors and lengths to the launch's maxima, so
+// inconsistent offsets can give wrong results but never an access outside
+// the tensors.  A fixed-length batch is left as it is.
+__device__ __forceinline__ void bind_seq(AttnArgs& a, int b) {
+  if (!a.cu_q) return;
+  const int q0 = min(max(a.cu_q[b], 0), a.total_q);
+  const int q1 = min(max(a.cu_q[b + 1], q0), a.total_q);
+  const int k0 = min(max(a.cu_k[b], 0), a.total_k);
+  const int k1 = min(max(a.cu_k[b + 1], k0), a.total_k);
+  const int64_t e = a.dtype == kF32 ? 4 : 2;
+  auto adv = [e](const void* p, int64_t rows, int64_t sn) -> const void* {
+    return p ? static_cast<const char*>(p) + rows * sn * e : p;
+  };
+  a.q = adv(a.q, q0, a.q_sn);
+  a.dq = const_cast<void*>(adv(a.dq, q0, a.q_sn));
+  a.o = const_cast<void*>(adv(a.o, q0, a.o_sn));
+  a.dout = adv(a.dout, q0, a.o_sn);
+  a.k = adv(a.k, k0, a.k_sn);
+  a.dk = const_cast<void*>(adv(a.dk, k0, a.k_sn));
+  a.v = adv(a.v, k0, a.v_sn);
+  a.dv = const_cast<void*>(adv(a.dv, k0, a.v_sn));
+  a.lse += q0;
+  if (a.dsum) a.dsum += q0 + 128 * (int64_t)b;
+  if (a.lse2) a.lse2 += q0 + 128 * (int64_t)b;
+  a.q_sb = a.k_sb = a.v_sb = a.o_sb = 0;
+  a.lse_sb = a.ws_sb = 0;
+  a.Nq = min(q1 - q0, a.Nq);
+  a.Nk = min(k1 - k0, a.Nk);
+  a.delta = a.Nk - a.Nq;
+}
 
 // Launch arguments of attention against a KV cache (decode.hip).
 struct KvArgs {

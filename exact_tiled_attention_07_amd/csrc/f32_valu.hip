@@ -121,6 +121,8 @@ __global__ __launch_bounds__(256) void f32_fwd_kernel(AttnArgs a) {
   const int b = blockIdx.x / (n_qt * a.Hq);
   const int hk = hq / a.G;
   const int q0 = qt * kT;
+  bind_seq(a, b);
+  if (q0 >= a.Nq) return;  // past the end of a shorter packed sequence (whole workgroup)
   const float* Qp = static_cast<const float*>(a.q) + b * a.q_sb + hq * a.q_sh;
   const float* Kp = static_cast<const float*>(a.k) + b * a.k_sb + hk * a.k_sh;
   const float* Vp = static_cast<const float*>(a.v) + b * a.v_sb + hk * a.v_sh;
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256) void f32_fwd_kernel(AttnArgs a) {
         if (cidx < a.D) Op[(int64_t)r * a.o_sn + cidx] = (l[ii] > 0.0) ? (float)(o[ii][jj] / l[ii]) : 0.f;
       }
       if (tc == 0)
-        a.lse[((int64_t)b * a.Hq + hq) * a.Nq + r] =
+        a.lse[b * a.lse_sb + hq * a.lse_sh + r] =
             (l[ii] > 0.0) ? (float)(m[ii] * a.scale + log(l[ii])) : -INFINITY;
     }
   }
@@ -212,6 +214,8 @@ __global__ __launch_bounds__(256) void f32_bwd_dq_kernel(AttnArgs a) {
   const int b = blockIdx.x / (n_qt * a.Hq);
   const int hk = hq / a.G;
   const int q0 = qt * kT;
+  bind_seq(a, b);
+  if (q0 >= a.Nq) return;  // past the end of a shorter packed sequence (whole workgroup)
   const float* Qp = static_cast<const float*>(a.q) + b * a.q_sb + hq * a.q_sh;
   const float* dOp = static_cast<const float*>(a.dout) + b * a.o_sb + hq * a.o_sh;
   const float* Kp = static_cast<const float*>(a.k) + b * a.k_sb + hk * a.k_sh;
@@ -227,8 +231,8 @@ __global__ __launch_bounds__(256) void f32_bwd_dq_kernel(AttnArgs a) {
     const int r = q0 + tr + 16 * ii;
     lo[ii] = key_lo(a, r);
     hi[ii] = key_hi(a, r);
-    const int64_t ri = ((int64_t)b * a.Hq + hq) * a.Nq + r;
-    const int64_t rp = ((int64_t)b * a.Hq + hq) * ((a.Nq + 127) / 128 * 128) + r;  // padded row index
+    const int64_t ri = b * a.lse_sb + hq * a.lse_sh + r;
+    const int64_t rp = b * a.ws_sb + hq * a.ws_sh + r;  // workspace row
     const float L = (r < a.Nq) ? a.lse[ri] : -INFINITY;
     lse2[ii] = (L == -INFINITY) ? INFINITY : (double)L * 1.4426950408889634;
     dsum[ii] = (r < a.Nq) ? (double)a.dsum[rp] : 0.0;
@@ -280,6 +284,8 @@ __global__ __launch_bounds__(256) void f32_bwd_dkdv_kernel(AttnArgs a) {
   const int hk = (blockIdx.x / n_kt) % a.Hkv;
   const int b = blockIdx.x / (n_kt * a.Hkv);
   const int k0 = kt * kT;
+  bind_seq(a, b);
+  if (k0 >= a.Nk) return;  // past the end of a shorter packed sequence (whole workgroup)
   const float* Kp = static_cast<const float*>(a.k) + b * a.k_sb + hk * a.k_sh;
   const float* Vp = static_cast<const float*>(a.v) + b * a.v_sb + hk * a.v_sh;
   load_rows_f32<DP, P>(Ks, Kp, a.k_sn, k0, a.Nk, a.D, tid);
@@ -300,8 +306,8 @@ __global__ __launch_bounds__(256) void f32_bwd_dkdv_kernel(AttnArgs a) {
     const int hq = hk * a.G + g;
     const float* Qp = static_cast<const float*>(a.q) + b * a.q_sb + hq * a.q_sh;
     const float* dOp = static_cast<const float*>(a.dout) + b * a.o_sb + hq * a.o_sh;
-    const int64_t rbase = ((int64_t)b * a.Hq + hq) * a.Nq;
-    const int64_t pbase = ((int64_t)b * a.Hq + hq) * ((a.Nq + 127) / 128 * 128);  // padded rows
+    const int64_t rbase = b * a.lse_sb + hq * a.lse_sh;
+    const int64_t pbase = b * a.ws_sb + hq * a.ws_sh;  // workspace rows
     for (int t = t_lo; t <= t_hi; ++t) {
       const int i0 = t * kT;
       __syncthreads();

@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <climits>
 #include <mutex>
 #include <string>
 
@@ -143,6 +144,11 @@ fa::AttnArgs make_args(const fa_params* p) {
   a.wr = p->window_right;
   a.delta = (int32_t)(p->seqlen_k - p->seqlen_q);
   a.xcd_remap = 1;
+  const int64_t nq_pad = (p->seqlen_q + 127) / 128 * 128;
+  a.lse_sb = p->nheads_q * p->seqlen_q;
+  a.lse_sh = p->seqlen_q;
+  a.ws_sb = p->nheads_q * nq_pad;
+  a.ws_sh = nq_pad;
   return a;
 }
 
@@ -209,6 +215,54 @@ size_t kv_workspace_bytes(const fa_kvcache_params* kp) {
   return ((n + 255) / 256) * 256;
 }
 
+
+// ----------------------------------------------------------------------------
+// Packed variable-length batches.
+// ----------------------------------------------------------------------------
+fa_status check_varlen(const fa_varlen_params* vp, fa_params* base) {
+  if (!vp) return fail(FA_ERR_INVALID_ARG, "params is NULL");
+  *base = vp->base;
+  base->q_strides[0] = base->k_strides[0] = base->v_strides[0] = base->o_strides[0] = 0;  // ignored
+  fa_status s = check_params(base);
+  if (s != FA_OK) return s;
+  if (vp->total_q < 0 || vp->total_k < 0)
+    return fail(FA_ERR_INVALID_ARG, "total_q / total_k must be >= 0 (got %lld, %lld)", (long long)vp->total_q,
+                (long long)vp->total_k);
+  if (vp->total_q > INT32_MAX || vp->total_k > INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "packed tensors above 2^31 - 1 rows are not supported");
+  return FA_OK;
+}
+
+fa_status check_offsets(const int32_t* cu, const char* name, bool needed) {
+  if (!needed) return FA_OK;
+  if (!cu) return fail(FA_ERR_INVALID_ARG, "%s is NULL", name);
+  if ((reinterpret_cast<uintptr_t>(cu) & 3u) != 0) return fail(FA_ERR_UNSUPPORTED, "%s is not 4-byte aligned", name);
+  return FA_OK;
+}
+
+// Row statistics of the backward: nheads_q * (total_q + 128 * batch) floats
+// per array (every sequence keeps up to 127 padding rows after its own).
+size_t varlen_ws_rows(const fa_params* p, const fa_varlen_params* vp) {
+  return (size_t)p->nheads_q * (size_t)(vp->total_q + 128 * p->batch);
+}
+size_t varlen_ws_bytes(const fa_params* p, const fa_varlen_params* vp) {
+  const size_t n = 2 * varlen_ws_rows(p, vp) * sizeof(float);
+  return ((n + 255) / 256) * 256;
+}
+
+fa::AttnArgs make_varlen_args(const fa_params* p, const fa_varlen_params* vp, const int32_t* cu_q,
+                              const int32_t* cu_k) {
+  fa::AttnArgs a = make_args(p);
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.total_q = (int32_t)vp->total_q;
+  a.total_k = (int32_t)vp->total_k;
+  a.lse_sb = 0;
+  a.lse_sh = vp->total_q;
+  a.ws_sb = 0;
+  a.ws_sh = vp->total_q + 128 * p->batch;
+  return a;
+}
 }  // namespace
 
 extern "C" {
@@ -311,6 +365,88 @@ fa_status fa_bwd_stage(const fa_params* params, int stage, const void* dout, con
     default: return fail(FA_ERR_INVALID_ARG, "unknown backward stage %d", stage);
   }
   return run_bwd(params, mask, dout, q, k, v, o, lse, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_fwd_varlen(const fa_varlen_params* params, const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o, float* lse,
+                        void* stream) {
+  fa_params p;
+  fa_status s = check_varlen(params, &p);
+  if (s != FA_OK) return s;
+  const bool nonempty = p.batch > 0 && params->total_q > 0 && p.seqlen_q > 0;
+  const bool kv_nonempty = nonempty && params->total_k > 0 && p.seqlen_k > 0;
+  if ((s = check_ptr(q, "q", nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(k, "k", kv_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(v, "v", kv_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(o, "o", nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(lse, "lse", nonempty)) != FA_OK) return s;
+  if ((s = check_offsets(cu_seqlens_q, "cu_seqlens_q", nonempty)) != FA_OK) return s;
+  if ((s = check_offsets(cu_seqlens_k, "cu_seqlens_k", nonempty)) != FA_OK) return s;
+  if (nonempty && (o == q || o == k || o == v)) return fail(FA_ERR_INVALID_ARG, "o must not alias q, k or v");
+  if (!nonempty) return FA_OK;
+  if ((s = check_device()) != FA_OK) return s;
+  fa::AttnArgs a = make_varlen_args(&p, params, cu_seqlens_q, cu_seqlens_k);
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = (p.dtype == FA_F32) ? fa::launch_fwd_f32(a, st) : fa::launch_fwd_mfma(a, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+fa_status fa_bwd_varlen_workspace_size(const fa_varlen_params* params, size_t* bytes) {
+  fa_params p;
+  fa_status s = check_varlen(params, &p);
+  if (s != FA_OK) return s;
+  if (!bytes) return fail(FA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = varlen_ws_bytes(&p, params);
+  return FA_OK;
+}
+
+fa_status fa_bwd_varlen(const fa_varlen_params* params, const void* dout, const void* q, const void* k,
+                        const void* v, const void* o, const float* lse, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  fa_params p;
+  fa_status s = check_varlen(params, &p);
+  if (s != FA_OK) return s;
+  const bool q_nonempty = p.batch > 0 && params->total_q > 0 && p.seqlen_q > 0;
+  const bool kv_nonempty = p.batch > 0 && params->total_k > 0 && p.seqlen_k > 0;
+  if ((s = check_ptr(dout, "dout", q_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(q, "q", q_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(k, "k", kv_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(v, "v", kv_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(o, "o", q_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(lse, "lse", q_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(dq, "dq", q_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(dk, "dk", kv_nonempty)) != FA_OK) return s;
+  if ((s = check_ptr(dv, "dv", kv_nonempty)) != FA_OK) return s;
+  if ((s = check_offsets(cu_seqlens_q, "cu_seqlens_q", q_nonempty || kv_nonempty)) != FA_OK) return s;
+  if ((s = check_offsets(cu_seqlens_k, "cu_seqlens_k", q_nonempty || kv_nonempty)) != FA_OK) return s;
+  const size_t need = varlen_ws_bytes(&p, params);
+  if (need > 0) {
+    if ((s = check_ptr(workspace, "workspace", true)) != FA_OK) return s;
+    if (workspace_bytes < need)
+      return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  }
+  if (q_nonempty || kv_nonempty) {
+    const void* outs[3] = {dq, dk, dv};
+    const void* ins[6] = {dout, q, k, v, o, lse};
+    for (const void* x : outs)
+      for (const void* y : ins)
+        if (x && x == y) return fail(FA_ERR_INVALID_ARG, "gradient outputs must not alias the inputs");
+  }
+  if (!q_nonempty && !kv_nonempty) return FA_OK;
+  if ((s = check_device()) != FA_OK) return s;
+  fa::AttnArgs a = make_varlen_args(&p, params, cu_seqlens_q, cu_seqlens_k);
+  a.q = q; a.k = k; a.v = v; a.o = const_cast<void*>(o); a.lse = const_cast<float*>(lse);
+  a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dsum = static_cast<float*>(workspace);
+  a.lse2 = a.dsum + varlen_ws_rows(&p, params);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      (p.dtype == FA_F32) ? fa::launch_bwd_f32(a, st, fa::kStageAll) : fa::launch_bwd_mfma(a, st, fa::kStageAll);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
 }
 
 fa_status fa_fwd_kvcache_workspace_size(const fa_kvcache_params* params, size_t* bytes) {

@@ -209,6 +209,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int hq = hk * a.G + it.sub;
   const int q0 = it.tile * BM;
   const int qrow = q0 + wave * 32 + l32;  // the query of this lane's column
+  bind_seq(a, b);
+  if (q0 >= a.Nq) return;  // past the end of a shorter packed sequence (whole workgroup)
 
   Ctx x;
   x.kbuf = kbuf;
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     if (hf == 0)
-      a.lse[((int64_t)b * a.Hq + hq) * a.Nq + qrow] = (lt > 0.f) ? (x.mref * a.scale + logf(lt)) : -INFINITY;
+      a.lse[b * a.lse_sb + hq * a.lse_sh + qrow] = (lt > 0.f) ? (x.mref * a.scale + logf(lt)) : -INFINITY;
   }
 }
 

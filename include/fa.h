@@ -164,6 +164,54 @@ fa_status fa_bwd_stage(const fa_params* params, int stage, const void* dout, con
                        void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Packed variable-length batches ([P4] section "上手 FlashAttention 的三步走":
+ * when the sequences of a batch differ in length, the varlen interfaces take
+ * them packed one after another instead of padded).
+ *
+ * Sequence b (0 <= b < base.batch) is rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ * of q, o, dout, dq (each (total_q, nheads_q, headdim)) and rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k, v, dk, dv (each (total_k,
+ * nheads_kv, headdim)).  Each sequence is attended on its own, exactly as one
+ * batch entry of fa_fwd / fa_bwd with its own lengths (masks aligned to the
+ * end of its own keys).
+ *
+ * base: batch = number of sequences; seqlen_q / seqlen_k = upper bounds of
+ *   the sequence lengths (they size the launch; longer sequences are cut to
+ *   them); the other fields as for fa_fwd.  strides[0] (the batch axis) is
+ *   ignored; strides[1] is the row stride and strides[2] the head stride of
+ *   the packed tensors.
+ * total_q, total_k: rows of the packed tensors (at most 2^31 - 1).
+ * cu_seqlens_q, cu_seqlens_k: int32 DEVICE arrays of batch + 1 prefix offsets,
+ *   cu[0] = 0, nondecreasing, cu[batch] <= total.  They are read on the
+ *   device: offsets are clamped to [0, total] and lengths to the bounds
+ *   above, so inconsistent values give unspecified results but never an
+ *   access outside the tensors.  Rows outside every sequence are not written.
+ * lse: float32 (nheads_q, total_q): lse[h * total_q + row].
+ */
+typedef struct {
+  fa_params base;
+  int64_t total_q;
+  int64_t total_k;
+} fa_varlen_params;
+
+/* Forward over a packed batch: o and lse as fa_fwd, per sequence. */
+fa_status fa_fwd_varlen(const fa_varlen_params* params, const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o, float* lse,
+                        void* stream);
+
+/* Bytes of workspace fa_bwd_varlen needs: two float32 arrays of
+ * nheads_q * (total_q + 128 * batch) entries, rounded up to 256 bytes. */
+fa_status fa_bwd_varlen_workspace_size(const fa_varlen_params* params, size_t* bytes);
+
+/* Backward over a packed batch: dq, dk, dv as fa_bwd, per sequence (dq has
+ * q's strides, dk k's, dv v's, dout o's).  Key rows of sequences without
+ * queries get zero gradients. */
+fa_status fa_bwd_varlen(const fa_varlen_params* params, const void* dout, const void* q, const void* k,
+                        const void* v, const void* o, const float* lse, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, void* dq, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
  * Attention against a KV cache (incremental decoding, [P4] section
  * "增量解码场景flash_attn_with_kvcache": new keys and values are appended to
  * the cache in place, cache_seqlens gives each batch entry's valid length,
@@ -225,6 +273,12 @@ const char* fa_last_error(void);
 
 /* FA_VERSION of the built library. */
 int fa_version(void);
+
+/* Packed Q/K/V ([P4] section "上手 FlashAttention 的三步走": q, k and v stored
+ * in one tensor) need no entry point of their own: a (batch, seqlen, 3, nheads,
+ * headdim) tensor gives q, k and v as strided views (head stride headdim,
+ * sequence stride 3 * nheads * headdim) for fa_fwd / fa_bwd, and dq, dk, dv can
+ * be the matching views of one packed gradient tensor. */
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -17,6 +17,8 @@ Sources (the web pages this method is taken from, cited by title and section):
 * [P4] same page, section "增量解码场景flash_attn_with_kvcache" (new keys and
   values appended to a cache in place, cache_seqlens as each batch entry's valid
   length) -- ``kvcache.py``.
+* [P4] same page, section "上手 FlashAttention 的三步走" (the varlen interfaces
+  for batches of sequences of different lengths) -- ``varlen.py``.
 * [P5] "AI模型推理优化Flash Attention原理" (52runoob.com) -- section "先搞清楚原理"
   (the standard_attention listing: scores scaled by one over the square root of
   the head dimension, softmax over the key axis, product with V).
@@ -41,5 +43,7 @@ from .attention import (  # noqa: F401
 )
 from .kvcache import ALL_FUNCTIONS as _KVCACHE_FUNCTIONS
 from .kvcache import kvcache_fwd  # noqa: F401
+from .varlen import ALL_FUNCTIONS as _VARLEN_FUNCTIONS
+from .varlen import attention_bwd_varlen, attention_fwd_varlen  # noqa: F401
 
-ALL_FUNCTIONS = _ATTENTION_FUNCTIONS + _KVCACHE_FUNCTIONS
+ALL_FUNCTIONS = _ATTENTION_FUNCTIONS + _KVCACHE_FUNCTIONS + _VARLEN_FUNCTIONS

@@ -35,7 +35,8 @@ def header_functions():
 def test_header_declares_expected_entry_points():
     assert header_functions() == sorted(
         ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd_kvcache",
-         "fa_fwd_kvcache_workspace_size", "fa_status_string", "fa_last_error", "fa_version"])
+         "fa_fwd_kvcache_workspace_size", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
+         "fa_status_string", "fa_last_error", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -47,7 +48,8 @@ def test_library_exports_every_declared_symbol(lib):
         assert name in N.SIGNATURES
 
 
-@pytest.mark.parametrize("cname,ctype", [("fa_params", N.FaParams), ("fa_kvcache_params", N.FaKvParams)])
+@pytest.mark.parametrize("cname,ctype", [("fa_params", N.FaParams), ("fa_kvcache_params", N.FaKvParams),
+                                         ("fa_varlen_params", N.FaVarlenParams)])
 def test_struct_layout_matches_c(tmp_path, cname, ctype):
     fields = [f for f, _ in ctype._fields_]
     src = ["#include <stdio.h>", "#include <stddef.h>", '#include "fa.h"', "int main(void){",
@@ -372,3 +374,74 @@ def test_python_kvcache_binding_rejects_cpu_tensors():
     c = torch.zeros(1, 32, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         fa.fwd_kvcache(q, c, c, torch.zeros(1, dtype=torch.int32))
+
+
+# --------------------------------------------------------------------------
+# fa_fwd_varlen / fa_bwd_varlen: host-side validation and workspace size.
+# --------------------------------------------------------------------------
+CQ, CK = 0x300000, 0x310000
+
+
+def vl_params(total_q=100, total_k=120, **kw):
+    """3 packed sequences, Hq=4, Hkv=2, d=64, max lengths 64; strides[0] deliberately garbage."""
+    base = dict(batch=3, q_strides=(12345, 4 * 64, 64), o_strides=(7, 4 * 64, 64), k_strides=(3, 2 * 64, 64),
+                v_strides=(1, 2 * 64, 64))
+    base.update(kw)
+    p = N.FaVarlenParams()
+    p.base = params(**base)
+    p.total_q, p.total_k = total_q, total_k
+    return p
+
+
+def call_fwd_vl(lib, p, q=A, k=B_, v=C, cq=CQ, ck=CK, o=O, lse=L):
+    pp = ctypes.byref(p) if p is not None else None
+    return lib.fa_fwd_varlen(pp, q, k, v, cq, ck, o, lse, None)
+
+
+def call_bwd_vl(lib, p, ws=W, ws_bytes=1 << 30, cq=CQ, ck=CK, dq=0x70000, dk=0x80000, dv=0x90000):
+    return lib.fa_bwd_varlen(ctypes.byref(p), 0xA0000, A, B_, C, O, L, cq, ck, dq, dk, dv, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("name,kw", INVALID, ids=[x[0] for x in INVALID])
+def test_varlen_invalid_arguments(lib, name, kw):
+    assert call_fwd_vl(lib, vl_params(**kw)) == N.FA_ERR_INVALID_ARG
+    assert call_bwd_vl(lib, vl_params(**kw)) == N.FA_ERR_INVALID_ARG
+
+
+def test_varlen_specific_validation(lib):
+    assert call_fwd_vl(lib, None) == N.FA_ERR_INVALID_ARG
+    assert call_fwd_vl(lib, vl_params(total_q=-1)) == N.FA_ERR_INVALID_ARG
+    assert call_fwd_vl(lib, vl_params(total_k=1 << 31)) == N.FA_ERR_UNSUPPORTED
+    assert call_fwd_vl(lib, vl_params(), cq=None) == N.FA_ERR_INVALID_ARG
+    assert b"cu_seqlens_q" in lib.fa_last_error()
+    assert call_fwd_vl(lib, vl_params(), ck=CK + 2) == N.FA_ERR_UNSUPPORTED
+    assert call_fwd_vl(lib, vl_params(), o=A) == N.FA_ERR_INVALID_ARG
+    assert call_bwd_vl(lib, vl_params(), cq=None) == N.FA_ERR_INVALID_ARG
+    assert call_bwd_vl(lib, vl_params(), dk=A) == N.FA_ERR_INVALID_ARG
+    # strides[0] is ignored: the garbage batch strides above are accepted,
+    # while a bad row stride is not.
+    assert call_fwd_vl(lib, vl_params(k_strides=(0, 2 * 64, 68))) == N.FA_ERR_UNSUPPORTED
+
+
+def test_varlen_workspace_size(lib):
+    p = vl_params()
+    n = ctypes.c_size_t()
+    assert lib.fa_bwd_varlen_workspace_size(ctypes.byref(p), ctypes.byref(n)) == N.FA_OK
+    # two float32 arrays of nheads_q * (total_q + 128 * batch)
+    assert n.value == ((2 * 4 * (100 + 128 * 3) * 4 + 255) // 256) * 256
+    assert lib.fa_bwd_varlen_workspace_size(ctypes.byref(p), None) == N.FA_ERR_INVALID_ARG
+    assert call_bwd_vl(lib, p, ws_bytes=n.value - 4) == N.FA_ERR_INVALID_ARG
+    assert b"workspace" in lib.fa_last_error()
+
+
+def test_varlen_empty_problems_return_ok_without_device(lib):
+    p = vl_params(total_q=0, total_k=0)
+    assert call_fwd_vl(lib, p, q=None, k=None, v=None, cq=None, ck=None, o=None, lse=None) == N.FA_OK
+    assert lib.fa_bwd_varlen(ctypes.byref(vl_params(batch=0, total_q=0, total_k=0)), None, None, None, None,
+                             None, None, None, None, None, None, None, W, 1 << 20, None) == N.FA_OK
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-GPU error path")
+def test_varlen_valid_call_without_gpu_reports_hip_error(lib):
+    assert call_fwd_vl(lib, vl_params()) == N.FA_ERR_HIP
+    assert call_bwd_vl(lib, vl_params()) == N.FA_ERR_HIP
