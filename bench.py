@@ -83,14 +83,14 @@ def flops(w):
 
 # HBM bytes per launch of the dK/dV kernel on the bench workload, from two
 # rocprofv3 --pmc runs of "python3 bench.py --steps 2 --warmup 1
-# --no-cpu-baseline" (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
+# --no-cpu-baseline --decode-calls 5" (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
 # scaled by the factor that the same counter needs to read 512 MiB for the
 # plain copy of "python3 bench.py --copy-probe".  They describe the kernel
 # built from the sources whose SHA-256 is recorded here and are reported as
 # null for any other source.
 DKDV_TRAFFIC = {
-    "sources_sha256": "e8fa1f20f4912f66b9a2a6ac9f8b0e066259c7ca710b6cbf460608f0f761ff51",
-    "bytes_per_launch": 2398479586,
+    "sources_sha256": "1423a15eeb58e31bf3d1d4d36d80ad5a2cd7e095ee345cf22409d1b81c1d4988",
+    "bytes_per_launch": 2261461327,
 }
 
 
