@@ -41,6 +41,10 @@ class FaParams(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("window_left", ctypes.c_int32),
         ("window_right", ctypes.c_int32),
+        ("alibi_slopes", ctypes.c_void_p),
+        ("alibi_batch_stride", ctypes.c_int64),
+        ("softcap", ctypes.c_float),
+        ("reserved_mod", ctypes.c_int32),
     ]
 
 
@@ -135,7 +139,23 @@ def _strides3(t):
     return _I64x3(s[0], s[1], s[2])
 
 
-def make_params(q, k, v, o, *, causal=False, window_size=(-1, -1), scale=None):
+def _set_modifiers(p, nheads_q, batch, alibi_slopes, softcap):
+    """Score modifiers: alibi_slopes a float32 GPU tensor (nheads_q,) or
+    (batch, nheads_q) (kept alive by the caller for the call), softcap >= 0."""
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_cuda or not alibi_slopes.is_contiguous():
+            raise ValueError("alibi_slopes must be a contiguous float32 GPU tensor")
+        if tuple(alibi_slopes.shape) == (nheads_q,):
+            p.alibi_batch_stride = 0
+        elif tuple(alibi_slopes.shape) == (batch, nheads_q):
+            p.alibi_batch_stride = nheads_q
+        else:
+            raise ValueError(f"alibi_slopes must be ({nheads_q},) or ({batch}, {nheads_q})")
+        p.alibi_slopes = alibi_slopes.data_ptr()
+    p.softcap = float(softcap)
+
+
+def make_params(q, k, v, o, *, causal=False, window_size=(-1, -1), scale=None, alibi_slopes=None, softcap=0.0):
     """FaParams for tensors shaped (batch, seqlen, nheads, headdim)."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (batch, seqlen, nheads, headdim)")
@@ -162,6 +182,7 @@ def make_params(q, k, v, o, *, causal=False, window_size=(-1, -1), scale=None):
     p.scale = (1.0 / math.sqrt(d)) if scale is None else float(scale)
     p.causal = 1 if causal else 0
     p.window_left, p.window_right = int(wl), int(wr)
+    _set_modifiers(p, hq, b, alibi_slopes, softcap)
     return p
 
 
@@ -179,10 +200,13 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(None)
 
 
-def fwd(q, k, v, *, causal=False, window_size=(-1, -1), scale=None, out=None, lse=None):
+def fwd(q, k, v, *, causal=False, window_size=(-1, -1), scale=None, out=None, lse=None, alibi_slopes=None,
+        softcap=0.0):
     """Exact attention forward: returns (o, lse).
 
     q (B, Nq, Hq, d); k, v (B, Nk, Hkv, d); o like q; lse float32 (B, Hq, Nq).
+    alibi_slopes (float32 GPU tensor (Hq,) or (B, Hq)) and softcap are the
+    optional score modifiers of include/fa.h.
     """
     _require_gpu(q, k, v)
     lib = load_library()
@@ -190,7 +214,8 @@ def fwd(q, k, v, *, causal=False, window_size=(-1, -1), scale=None, out=None, ls
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
-    p = make_params(q, k, v, out, causal=causal, window_size=window_size, scale=scale)
+    p = make_params(q, k, v, out, causal=causal, window_size=window_size, scale=scale, alibi_slopes=alibi_slopes,
+                    softcap=softcap)
     with torch.cuda.device(q.device):
         _check(lib.fa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q.device)))
     return out, lse
@@ -204,7 +229,7 @@ def bwd_workspace_size(params):
 
 
 def bwd(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1), scale=None,
-        dq=None, dk=None, dv=None, workspace=None, stage=None):
+        dq=None, dk=None, dv=None, workspace=None, stage=None, alibi_slopes=None, softcap=0.0):
     """Exact attention backward: returns (dq, dk, dv) of L = sum(out * dout).
 
     dout uses out's layout; dq gets q's strides, dk/dv get k's and v's.
@@ -221,7 +246,8 @@ def bwd(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1), scale=No
     if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[0], q.shape[2], q.shape[1]) \
             or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (batch, nheads_q, seqlen_q) tensor")
-    p = make_params(q, k, v, out, causal=causal, window_size=window_size, scale=scale)
+    p = make_params(q, k, v, out, causal=causal, window_size=window_size, scale=scale, alibi_slopes=alibi_slopes,
+                    softcap=softcap)
     dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if dq is None else dq
     dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device) if dk is None else dk
     dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device) if dv is None else dv
@@ -242,7 +268,7 @@ def bwd(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1), scale=No
 
 
 def make_varlen_params(q, k, v, o, max_seqlen_q, max_seqlen_k, *, causal=False, window_size=(-1, -1),
-                       scale=None):
+                       scale=None, alibi_slopes=None, softcap=0.0, batch=0):
     """FaVarlenParams for packed tensors q/o (total_q, Hq, d), k/v (total_k, Hkv, d)."""
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or o.dim() != 3:
         raise ValueError("packed q, k, v, o must be 3-D (total, nheads, headdim)")
@@ -271,6 +297,8 @@ def make_varlen_params(q, k, v, o, max_seqlen_q, max_seqlen_k, *, causal=False, 
     b.causal = 1 if causal else 0
     b.window_left, b.window_right = int(wl), int(wr)
     p.total_q, p.total_k = q.shape[0], k.shape[0]
+    b.batch = int(batch)
+    _set_modifiers(b, q.shape[1], int(batch), alibi_slopes, softcap)
     return p
 
 
@@ -280,7 +308,7 @@ def _check_offsets(cu, name):
 
 
 def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,
-               window_size=(-1, -1), scale=None, out=None, lse=None):
+               window_size=(-1, -1), scale=None, out=None, lse=None, alibi_slopes=None, softcap=0.0):
     """Forward over a packed batch: returns (o, lse).
 
     q (total_q, Hq, d); k, v (total_k, Hkv, d); cu_seqlens_* int32 (batch + 1,)
@@ -298,8 +326,7 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, 
     if lse is None:
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
     p = make_varlen_params(q, k, v, out, max_seqlen_q, max_seqlen_k, causal=causal, window_size=window_size,
-                           scale=scale)
-    p.base.batch = cu_seqlens_q.numel() - 1
+                           scale=scale, alibi_slopes=alibi_slopes, softcap=softcap, batch=cu_seqlens_q.numel() - 1)
     with torch.cuda.device(q.device):
         _check(lib.fa_fwd_varlen(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
                                  _ptr(cu_seqlens_k), _ptr(out), _ptr(lse), _stream(q.device)))
@@ -314,7 +341,8 @@ def bwd_varlen_workspace_size(params):
 
 
 def bwd_varlen(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *,
-               causal=False, window_size=(-1, -1), scale=None, dq=None, dk=None, dv=None, workspace=None):
+               causal=False, window_size=(-1, -1), scale=None, dq=None, dk=None, dv=None, workspace=None,
+               alibi_slopes=None, softcap=0.0):
     """Backward over a packed batch: returns (dq, dk, dv) of L = sum(out * dout)."""
     _require_gpu(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k)
     _check_offsets(cu_seqlens_q, "cu_seqlens_q")
@@ -325,8 +353,7 @@ def bwd_varlen(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q
     if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[1], q.shape[0]) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (nheads_q, total_q) tensor")
     p = make_varlen_params(q, k, v, out, max_seqlen_q, max_seqlen_k, causal=causal, window_size=window_size,
-                           scale=scale)
-    p.base.batch = cu_seqlens_q.numel() - 1
+                           scale=scale, alibi_slopes=alibi_slopes, softcap=softcap, batch=cu_seqlens_q.numel() - 1)
     dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if dq is None else dq
     dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device) if dk is None else dk
     dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device) if dv is None else dv
@@ -344,9 +371,10 @@ def bwd_varlen(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q
 
 
 def make_kv_params(q, k_cache, v_cache, out, k_new=None, v_new=None, *, causal=False, window_size=(-1, -1),
-                   scale=None, num_splits=0):
+                   scale=None, num_splits=0, alibi_slopes=None, softcap=0.0):
     """FaKvParams: q/out (B, Nq, Hq, d), caches (B, capacity, Hkv, d), new rows like q with Hkv heads."""
-    base = make_params(q, k_cache, v_cache, out, causal=causal, window_size=window_size, scale=scale)
+    base = make_params(q, k_cache, v_cache, out, causal=causal, window_size=window_size, scale=scale,
+                       alibi_slopes=alibi_slopes, softcap=softcap)
     p = FaKvParams()
     p.base = base
     if (k_new is None) != (v_new is None):
@@ -372,7 +400,8 @@ def kvcache_workspace_size(params):
 
 
 def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, *, causal=False,
-                window_size=(-1, -1), scale=None, num_splits=0, out=None, lse=None, workspace=None):
+                window_size=(-1, -1), scale=None, num_splits=0, out=None, lse=None, workspace=None,
+                alibi_slopes=None, softcap=0.0):
     """Attention of q against a KV cache, appending k_new / v_new first: returns (o, lse).
 
     q (B, Nq, Hq, d); k_cache, v_cache (B, capacity, Hkv, d), updated in place
@@ -393,7 +422,7 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, *, c
     if lse is None:
         lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
     p = make_kv_params(q, k_cache, v_cache, out, k_new, v_new, causal=causal, window_size=window_size,
-                       scale=scale, num_splits=num_splits)
+                       scale=scale, num_splits=num_splits, alibi_slopes=alibi_slopes, softcap=softcap)
     need = kvcache_workspace_size(p)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -406,26 +435,28 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, *, c
 
 class _Attention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, causal, window_size, scale):
-        o, lse = fwd(q, k, v, causal=causal, window_size=window_size, scale=scale)
+    def forward(ctx, q, k, v, causal, window_size, scale, alibi_slopes, softcap):
+        o, lse = fwd(q, k, v, causal=causal, window_size=window_size, scale=scale, alibi_slopes=alibi_slopes,
+                     softcap=softcap)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.cfg = (causal, window_size, scale)
+        ctx.cfg = (causal, window_size, scale, alibi_slopes, softcap)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        causal, window_size, scale = ctx.cfg
+        causal, window_size, scale, alibi_slopes, softcap = ctx.cfg
         do = do.contiguous() if do.stride() != o.stride() else do
         if do.stride() != o.stride():
             do = torch.empty_strided(o.shape, o.stride(), dtype=o.dtype, device=o.device).copy_(do)
-        dq, dk, dv = bwd(do, q, k, v, o, lse, causal=causal, window_size=window_size, scale=scale)
-        return dq, dk, dv, None, None, None
+        dq, dk, dv = bwd(do, q, k, v, o, lse, causal=causal, window_size=window_size, scale=scale,
+                         alibi_slopes=alibi_slopes, softcap=softcap)
+        return dq, dk, dv, None, None, None, None, None
 
 
-def attention(q, k, v, *, causal=False, window_size=(-1, -1), scale=None):
+def attention(q, k, v, *, causal=False, window_size=(-1, -1), scale=None, alibi_slopes=None, softcap=0.0):
     """Differentiable exact attention over (batch, seqlen, nheads, headdim) tensors."""
-    return _Attention.apply(q, k, v, causal, tuple(window_size), scale)
+    return _Attention.apply(q, k, v, causal, tuple(window_size), scale, alibi_slopes, softcap)
 
 
 class _AttentionVarlen(torch.autograd.Function):

@@ -159,7 +159,7 @@ struct DkdvWsLayout {
   static constexpr int BYTES = OFF_RST + NSLOT * RST;
 };
 
-template <class T, int D, int BMQ>
+template <class T, int D, int BMQ, bool MOD>
 struct DkdvWs {
   using L = DkdvWsLayout<D, BMQ>;
   char* smem;  // [slot][Q tile, dO tile], [score wave][P, dS images], [slot][lse2, dsum]
@@ -300,6 +300,22 @@ struct DkdvWs {
     lds_barrier();  // the gradient waves have taken the previous item's P and dS
     if (w < n_items) {
       const int i0 = row_of(cu);
+      // Score modifiers; bit r of inside[qb] records whether the clamp passes
+      // the gradient of element [qb][r].
+      uint32_t inside[BMQ / 32];
+      if constexpr (MOD) {
+        const float slope_r = alibi_raw(a->alibi, a->alibi_sb, a->inv_scale, b, hk * a->G + cu.g);
+        const float base = (float)(i0 + a->delta - key + 4 * hf);  // i' - key of element [0][0]
+#pragma unroll
+        for (int qb = 0; qb < BMQ / 32; ++qb) {
+          inside[qb] = 0u;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            inside[qb] |= (fabsf(s[qb][r]) < a->cap ? 1u : 0u) << r;
+            s[qb][r] = mod_score(s[qb][r], a->cap, slope_r, base + (float)(32 * qb + 8 * (r >> 2) + (r & 3)));
+          }
+        }
+      }
       const int i_end = min(i0 + BMQ, a->Nq) - 1;
       const bool full = (key_lo(*a, i_end) <= k0) && (key_hi(*a, i0) >= k_last);
       if (!full) {
@@ -333,6 +349,7 @@ struct DkdvWs {
             const float pr = fast_exp2(fmaf(s[qb][r], c, -l4[r >> 2][r & 3]));
             pb[e] = pr;
             db_[e] = pr * (dp[qb][r] - d4[r >> 2][r & 3]);
+            if constexpr (MOD) db_[e] = ((inside[qb] >> r) & 1u) ? db_[e] : 0.f;
           }
           const int si = 2 * qb + tt;
           *reinterpret_cast<u32x4*>(pimg + si * 1024) =
@@ -402,7 +419,7 @@ struct DkdvWs {
   }
 };
 
-template <class T, int D, int BMQ>
+template <class T, int D, int BMQ, bool MOD>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_ws_kernel(AttnArgs a) {
   using L = DkdvWsLayout<D, BMQ>;
@@ -416,7 +433,7 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
   // Under a causal mask the first key tiles see the most queries: run them first.
   const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_kt, 1, false, a.xcd_remap);
 
-  DkdvWs<T, D, BMQ> x;
+  DkdvWs<T, D, BMQ, MOD> x;
   x.smem = smem;
   x.a = &a;
   x.b = it.unit / a.Hkv;
@@ -440,7 +457,7 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
   x.dd.init(x.kb, lane, a.o_sn);
 
   if (x.n_items > 0 && wave < L::KW) {
-    x.issue(typename DkdvWs<T, D, BMQ>::Cursor{0, 0}, 0);
+    x.issue(typename DkdvWs<T, D, BMQ, MOD>::Cursor{0, 0}, 0);
     wait_all_loads();
   }
   __syncthreads();
@@ -475,7 +492,7 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <class T, int D, int BN, int NW>
+template <class T, int D, int BN, int NW, bool MOD>
 struct DqCtx {
   static constexpr int TILE = BN * D;
   uint16_t* smem;  // [buf][K tile, V tile]
@@ -484,6 +501,7 @@ struct DqCtx {
   int64_t k_sn, v_sn;
   int Nk, t_hi, lo_i, hi_i, lo_max, hi_min, wave, hf;
   float c, lse2, dsum;
+  float cap, slope_r, dist0;  // score modifiers (MOD): clamp, raw slope, i' - 4*hf of this lane
   u32x4 qf[D / 16], df[D / 16];
   f32x16 dqa[D / 32];
   SwzOffsets<D> off;
@@ -524,7 +542,7 @@ struct DqCtx {
       }
     }
     const bool full = (j0 >= lo_max) && (j0 + BN - 1 <= hi_min);
-    if (!full) {
+    if (!MOD && !full) {  // with the modifiers the mask follows them, element by element below
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
@@ -544,8 +562,17 @@ struct DqCtx {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * tt + e;
-          const float pr = fast_exp2(fmaf(s[kb][r], c, -lse2));
-          ds[e] = pr * (dp[kb][r] - dsum);
+          float sv = s[kb][r], dv = dp[kb][r];
+          if constexpr (MOD) {
+            // Where the clamp blocks the gradient, dP is replaced by D, which
+            // makes dS = P * (dP - D) exactly 0.
+            if (!(fabsf(sv) < cap)) dv = dsum;
+            sv = mod_score(sv, cap, slope_r, dist0 - (float)(j0 + 32 * kb + 8 * (r >> 2) + (r & 3)));
+            const int kk = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (!full && (kk < lo_i || kk > hi_i)) sv = -INFINITY;
+          }
+          const float pr = fast_exp2(fmaf(sv, c, -lse2));
+          ds[e] = pr * (dv - dsum);
         }
         dsf[2 * kb + tt] = u32x4{T::pack(ds[0], ds[1]), T::pack(ds[2], ds[3]), T::pack(ds[4], ds[5]),
                                  T::pack(ds[6], ds[7])};
@@ -572,10 +599,10 @@ struct DqCtx {
   }
 };
 
-template <class T, int D, int BN, int NW>
+template <class T, int D, int BN, int NW, bool MOD>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_WPE, FA_DQ_WPE))) void bwd_dq_kernel(AttnArgs a) {
   constexpr int BM = NW * 32;
-  using Ctx = DqCtx<T, D, BN, NW>;
+  using Ctx = DqCtx<T, D, BN, NW, MOD>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * Ctx::TILE];
   static_assert(2 * 2 * Ctx::TILE * 2 <= 65536, "LDS offsets must fit the 16-bit immediate");
 
@@ -602,6 +629,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
   x.wave = wave;
   x.hf = hf;
   x.c = a.scale_log2;
+  if constexpr (MOD) {
+    x.cap = a.cap;
+    x.slope_r = alibi_raw(a.alibi, a.alibi_sb, a.inv_scale, b, hq);
+    x.dist0 = (float)(qrow + a.delta - 4 * hf);
+  }
   const uint16_t* Qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh;
   const uint16_t* dOp = static_cast<const uint16_t*>(a.dout) + b * a.o_sb + hq * a.o_sh;
   x.lse2 = INFINITY;
@@ -678,16 +710,24 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream, int stages
   const int n_kt = (a.Nk + WL::BNK - 1) / WL::BNK;
   const int64_t grid_kv = (int64_t)a.B * a.Hkv * n_kt;
   if (grid_kv > 0 && (stages & kStageDkdv)) {
-    hipLaunchKernelGGL((bwd_dkdv_ws_kernel<T, D, FA_DKDV_BMQ>), dim3((unsigned)grid_kv), dim3(WL::NW * 64), 0,
-                       stream, args);
+    if (a.mod)
+      hipLaunchKernelGGL((bwd_dkdv_ws_kernel<T, D, FA_DKDV_BMQ, true>), dim3((unsigned)grid_kv), dim3(WL::NW * 64),
+                         0, stream, args);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_ws_kernel<T, D, FA_DKDV_BMQ, false>), dim3((unsigned)grid_kv),
+                         dim3(WL::NW * 64), 0, stream, args);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int n_qt = (a.Nq + FA_DQ_NW * 32 - 1) / (FA_DQ_NW * 32);
   const int64_t grid_q = (int64_t)a.B * a.Hkv * n_qt * a.G;
   if (grid_q > 0 && (stages & kStageDq)) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, FA_DQ_BN, FA_DQ_NW>), dim3((unsigned)grid_q), dim3(FA_DQ_NW * 64),
-                       0, stream, args);
+    if (a.mod)
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, FA_DQ_BN, FA_DQ_NW, true>), dim3((unsigned)grid_q),
+                         dim3(FA_DQ_NW * 64), 0, stream, args);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, FA_DQ_BN, FA_DQ_NW, false>), dim3((unsigned)grid_q),
+                         dim3(FA_DQ_NW * 64), 0, stream, args);
     e = hipGetLastError();
   }
   return e;

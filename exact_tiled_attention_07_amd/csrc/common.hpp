@@ -58,7 +58,31 @@ struct AttnArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int32_t total_q, total_k;
+  // Score modifiers (kernels built with them only when mod != 0): slope of
+  // (b, h) at alibi[b * alibi_sb + h] (NULL: none); cap = softcap / scale in
+  // raw score units (+inf: none).
+  const float* alibi;
+  int64_t alibi_sb;
+  float cap;
+  float inv_scale;  // 1 / scale: turns a slope into raw score units
+  float softcap;    // the parameter itself (0: none), for the float64 path
+  int32_t mod;
 };
+
+// ---------------------------------------------------------------------------
+// Score modifiers ([P4] "FlashAttention 实战指南", section "进阶参数如何配置
+// causal、window_size 与 MQA/GQA": alibi_slopes decays scores with distance,
+// softcap truncates the logits to [-softcap, softcap]).  In raw units
+// (logit = scale * s): s is clamped to [-cap, cap] with cap = softcap/scale,
+// then slope/scale * |i' - j| is subtracted; masking comes after.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float mod_score(float s, float cap, float slope_raw, float dist) {
+  return fmaf(-slope_raw, fabsf(dist), fminf(fmaxf(s, -cap), cap));
+}
+// Slope of (b, h) in raw score units (0 without ALiBi).
+__device__ __forceinline__ float alibi_raw(const float* alibi, int64_t sb, float inv_scale, int b, int h) {
+  return alibi ? alibi[b * sb + h] * inv_scale : 0.f;
+}
 
 // Binds the arguments to batch entry b of a packed variable-length batch:
 // every pointer moves to the sequence's first row (the workspace rows to
@@ -120,6 +144,10 @@ struct KvArgs {
   int32_t n_rb;       // blocks of 32 packed query rows (G * Nq rows)
   int32_t n_split;    // waves of the split phase: B * Hkv * n_rb * S
   int32_t n_append;   // waves that copy the new rows into the cache
+  const float* alibi;  // score modifiers, as in AttnArgs (score_cap = softcap / scale)
+  int64_t alibi_sb;
+  float score_cap, inv_scale;
+  int32_t mod;
 };
 
 static constexpr float kLog2e = 1.4426950408889634f;

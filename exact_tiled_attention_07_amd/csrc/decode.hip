@@ -97,7 +97,7 @@ struct KvStage {
   u32x4 vr[CPL];
 };
 
-template <class T, int D, int DEPTH>
+template <class T, int D, int DEPTH, bool MOD>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES))) void kv_split_kernel(KvArgs k) {
   constexpr int NST = D / 16;  // 16-wide d steps
   constexpr int CPL = KvStage<D>::CPL;
@@ -176,6 +176,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
   SwzOffsets<D> off;
   off.init(lane);
   const float cs = k.scale_log2;
+  // Score modifiers: this lane's raw slope and i' - 4*hf (query aligned to the end of the keys).
+  float slope_r = 0.f, dist0 = 0.f;
+  if constexpr (MOD) {
+    slope_r = alibi_raw(k.alibi, k.alibi_sb, k.inv_scale, b, hq);
+    dist0 = (float)(i + Lk - k.Nq - 4 * hf);
+  }
 
   // Every K/V element is read once: the non-temporal hint keeps the stream
   // from displacing reusable lines (measured 10% faster on MI355X).
@@ -213,6 +219,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
 #pragma unroll
     for (int c = 0; c < NST; ++c) sv = T::mfma(off.row_chunk(reinterpret_cast<const char*>(kt), 0, c), qf[c], sv);
     const int j0 = 32 * t;
+    if constexpr (MOD) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sv[r] = mod_score(sv[r], k.score_cap, slope_r, dist0 - (float)(j0 + 8 * (r >> 2) + (r & 3)));
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = j0 + 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -359,8 +370,12 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(KvArgs k) {
 
 template <class T, int D>
 static hipError_t launch_kv_t(const KvArgs& k, hipStream_t stream) {
-  hipLaunchKernelGGL((kv_split_kernel<T, D, FA_KV_DEPTH>),
-                     dim3((unsigned)(k.n_split + k.n_append)), dim3(64), 0, stream, k);
+  if (k.mod)
+    hipLaunchKernelGGL((kv_split_kernel<T, D, FA_KV_DEPTH, true>), dim3((unsigned)(k.n_split + k.n_append)),
+                       dim3(64), 0, stream, k);
+  else
+    hipLaunchKernelGGL((kv_split_kernel<T, D, FA_KV_DEPTH, false>), dim3((unsigned)(k.n_split + k.n_append)),
+                       dim3(64), 0, stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)k.B * k.Hq * k.Nq;

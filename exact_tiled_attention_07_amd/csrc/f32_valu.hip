@@ -107,6 +107,23 @@ __device__ __forceinline__ void store_rows_f32(float* base, int64_t stride, int 
 
 }  // namespace
 
+// Score modifiers in float64 and raw units (logit = scale * s): s clamped to
+// +-softcap/scale, then slope/scale * |i' - j| subtracted (common.hpp).
+struct ModF64 {
+  bool on;
+  double cap, slope;
+  __device__ ModF64(const AttnArgs& a, int b, int h)
+      : on(a.mod != 0),
+        cap(a.softcap > 0.f ? (double)a.softcap / (double)a.scale : INFINITY),
+        slope(a.alibi ? (double)a.alibi[b * a.alibi_sb + h] / (double)a.scale : 0.0) {}
+  // Modified score of raw score s at distance i' - j.
+  __device__ __forceinline__ double apply(double s, int dist) const {
+    return fmin(fmax(s, -cap), cap) - slope * (double)abs(dist);
+  }
+  // Whether the clamp passes the gradient at raw score s.
+  __device__ __forceinline__ bool pass(double s) const { return fabs(s) < cap; }
+};
+
 // ---------------------------------------------------------------------------
 // Forward.
 // ---------------------------------------------------------------------------
@@ -145,6 +162,7 @@ __global__ __launch_bounds__(256) void f32_fwd_kernel(AttnArgs a) {
   const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
   const int t_lo = kv_lo / kT, t_hi = (kv_hi >= kv_lo) ? kv_hi / kT : t_lo - 1;
   const double c = (double)a.scale * 1.4426950408889634;
+  const ModF64 md(a, b, hq);
 
   for (int t = t_lo; t <= t_hi; ++t) {
     const int j0 = t * kT;
@@ -160,6 +178,7 @@ __global__ __launch_bounds__(256) void f32_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int key = j0 + tc + 16 * jj;
+        if (md.on) s[ii][jj] = md.apply(s[ii][jj], q0 + tr + 16 * ii + a.delta - key);
         if (key < lo[ii] || key > hi[ii]) s[ii][jj] = -INFINITY;
         mx = fmax(mx, s[ii][jj]);
       }
@@ -243,6 +262,7 @@ __global__ __launch_bounds__(256) void f32_bwd_dq_kernel(AttnArgs a) {
   const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
   const int t_lo = kv_lo / kT, t_hi = (kv_hi >= kv_lo) ? kv_hi / kT : t_lo - 1;
   const double c = (double)a.scale * 1.4426950408889634;
+  const ModF64 md(a, b, hq);
 
   for (int t = t_lo; t <= t_hi; ++t) {
     const int j0 = t * kT;
@@ -258,9 +278,14 @@ __global__ __launch_bounds__(256) void f32_bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int key = j0 + tc + 16 * jj;
+        bool pass = true;
+        if (md.on) {
+          pass = md.pass(s[ii][jj]);
+          s[ii][jj] = md.apply(s[ii][jj], q0 + tr + 16 * ii + a.delta - key);
+        }
         const bool vis = key >= lo[ii] && key <= hi[ii];
         const double p = vis ? (double)fast_exp2((float)(s[ii][jj] * c - lse2[ii])) : 0.0;
-        Ps[(tr + 16 * ii) * (kT + 1) + tc + 16 * jj] = (float)(p * (dp[ii][jj] - dsum[ii]));
+        Ps[(tr + 16 * ii) * (kT + 1) + tc + 16 * jj] = pass ? (float)(p * (dp[ii][jj] - dsum[ii])) : 0.f;
       }
     }
     __syncthreads();
@@ -304,6 +329,7 @@ __global__ __launch_bounds__(256) void f32_bwd_dkdv_kernel(AttnArgs a) {
 
   for (int g = 0; g < a.G; ++g) {
     const int hq = hk * a.G + g;
+    const ModF64 md(a, b, hq);
     const float* Qp = static_cast<const float*>(a.q) + b * a.q_sb + hq * a.q_sh;
     const float* dOp = static_cast<const float*>(a.dout) + b * a.o_sb + hq * a.o_sh;
     const int64_t rbase = b * a.lse_sb + hq * a.lse_sh;
@@ -333,10 +359,15 @@ __global__ __launch_bounds__(256) void f32_bwd_dkdv_kernel(AttnArgs a) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int key = k0 + tr + 16 * ii;
+          bool pass = true;
+          if (md.on) {
+            pass = md.pass(s[ii][jj]);
+            s[ii][jj] = md.apply(s[ii][jj], i + a.delta - key);
+          }
           const bool vis = key >= lo && key <= hi;
           const float p = vis ? fast_exp2((float)(s[ii][jj] * c - l2)) : 0.f;
           Ps[(tr + 16 * ii) * (kT + 1) + tc + 16 * jj] = p;
-          ds[ii][jj] = (float)((double)p * (dp[ii][jj] - dd));
+          ds[ii][jj] = pass ? (float)((double)p * (dp[ii][jj] - dd)) : 0.f;
         }
       }
       __syncthreads();

@@ -60,6 +60,12 @@ fa_status check_params(const fa_params* p) {
   if (p->window_left < -1 || p->window_right < -1)
     return fail(FA_ERR_INVALID_ARG, "window bounds must be >= -1 (got %d, %d)", p->window_left,
                 p->window_right);
+  if (!(std::isfinite(p->softcap) && p->softcap >= 0.f))
+    return fail(FA_ERR_INVALID_ARG, "softcap must be finite and >= 0 (0 = off)");
+  if (p->alibi_batch_stride < 0) return fail(FA_ERR_INVALID_ARG, "alibi_batch_stride must be >= 0");
+  if (p->reserved_mod != 0) return fail(FA_ERR_INVALID_ARG, "reserved_mod must be 0");
+  if (p->alibi_slopes && (reinterpret_cast<uintptr_t>(p->alibi_slopes) & 3u) != 0)
+    return fail(FA_ERR_UNSUPPORTED, "alibi_slopes is not 4-byte aligned");
   if (p->seqlen_q > kMaxSeq || p->seqlen_k > kMaxSeq || p->nheads_q > kMaxHeads || p->batch > kMaxBatch)
     return fail(FA_ERR_UNSUPPORTED, "sizes exceed this build's limits");
   if (p->batch * p->nheads_q * ((p->seqlen_q + 31) / 32) >= (int64_t(1) << 31) ||
@@ -144,6 +150,12 @@ fa::AttnArgs make_args(const fa_params* p) {
   a.wr = p->window_right;
   a.delta = (int32_t)(p->seqlen_k - p->seqlen_q);
   a.xcd_remap = 1;
+  a.alibi = p->alibi_slopes;
+  a.alibi_sb = p->alibi_batch_stride;
+  a.cap = p->softcap > 0.f ? p->softcap / p->scale : INFINITY;
+  a.inv_scale = 1.f / p->scale;
+  a.softcap = p->softcap;
+  a.mod = (p->alibi_slopes != nullptr || p->softcap > 0.f) ? 1 : 0;
   const int64_t nq_pad = (p->seqlen_q + 127) / 128 * 128;
   a.lse_sb = p->nheads_q * p->seqlen_q;
   a.lse_sh = p->seqlen_q;
@@ -518,6 +530,11 @@ fa_status fa_fwd_kvcache(const fa_kvcache_params* params, const void* q, void* k
   k.scale_log2 = p->scale * fa::kLog2e;
   k.causal = p->causal; k.wl = p->window_left; k.wr = p->window_right;
   k.append = k_new != nullptr;
+  k.alibi = p->alibi_slopes;
+  k.alibi_sb = p->alibi_batch_stride;
+  k.score_cap = p->softcap > 0.f ? p->softcap / p->scale : INFINITY;
+  k.inv_scale = 1.f / p->scale;
+  k.mod = (p->alibi_slopes != nullptr || p->softcap > 0.f) ? 1 : 0;
   k.S = (int32_t)S;
   k.n_rb = (int32_t)n_rb;
   k.n_split = (int32_t)n_split;

@@ -63,7 +63,7 @@ static constexpr float kLazyRescale = 8.0f;
 // whose last readers finished in interval 2m-1, and waits for them at the
 // end of interval 2m+1.
 // ---------------------------------------------------------------------------
-template <class T, int D, int BN>
+template <class T, int D, int BN, bool MOD>
 struct FwdPP {
   static constexpr int NW = 8, HALF = 4;
   static constexpr int TILE = BN * D;  // elements of one K or V tile
@@ -79,6 +79,7 @@ struct FwdPP {
   int vro[D / 32][2];  // per-lane LDS offsets of the transposing V reads
   DmaTile<D, BN, HALF> kd, vd;  // group A's shares of the K and V tile loads
   float mref, l;
+  float cap, slope_r, dist0;  // score modifiers (MOD): clamp, raw slope, i' - 4*hf of this lane
   f32x16 oacc[D / 32];
   f32x16 s[BN / 32];  // scores of tile m between its MFMA and softmax intervals
   u32x4 pf[BN / 16];  // P^T of tile m between its softmax and the next MFMA interval
@@ -143,6 +144,16 @@ struct FwdPP {
   __device__ __forceinline__ void softmax_interval(int m) {
     if (m < 0 || m >= n) return;
     const int j0 = (t_lo + m) * BN;
+    if constexpr (MOD) {
+      // s[kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4; dist0 = i' - 4*hf.
+      const float base = dist0 - (float)j0;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb][r] = mod_score(s[kb][r], cap, slope_r, base - (float)(32 * kb + 8 * (r >> 2) + (r & 3)));
+      }
+    }
     const bool full = (j0 >= lo_max) && (j0 + BN - 1 <= hi_min);
     if (!full) {
 #pragma unroll
@@ -189,9 +200,9 @@ struct FwdPP {
   }
 };
 
-template <class T, int D, int BN>
+template <class T, int D, int BN, bool MOD>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pp_kernel(AttnArgs a) {
-  using Ctx = FwdPP<T, D, BN>;
+  using Ctx = FwdPP<T, D, BN, MOD>;
   constexpr int NW = Ctx::NW, BM = NW * 32, TILE = Ctx::TILE;
   __shared__ __attribute__((aligned(16))) uint16_t kbuf[2 * TILE];
   __shared__ __attribute__((aligned(16))) uint16_t vbuf[2 * TILE];
@@ -224,6 +235,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   x.lane = lane;
   x.hf = hf;
   x.c = a.scale_log2;
+  if constexpr (MOD) {
+    x.cap = a.cap;
+    x.slope_r = alibi_raw(a.alibi, a.alibi_sb, a.inv_scale, b, hq);
+    x.dist0 = (float)(qrow + a.delta - 4 * hf);
+  }
   const uint16_t* Qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh;
 
   // Q as the B operand of S^T = K Q^T: lane holds d = 16*st + 8*hf + (0..7).
@@ -351,8 +367,11 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t stream) {
   if (total == 0) return hipSuccess;
   AttnArgs args = a;
   args.xcd_remap = a.xcd_remap && ((a.B * a.Hkv) % 8 == 0);
-  static_assert(NW == FwdPP<T, D, BN>::NW, "the forward runs 8 waves");
-  hipLaunchKernelGGL((fwd_pp_kernel<T, D, BN>), dim3((unsigned)total), dim3(NW * 64), 0, stream, args);
+  static_assert(NW == FwdPP<T, D, BN, false>::NW, "the forward runs 8 waves");
+  if (a.mod)
+    hipLaunchKernelGGL((fwd_pp_kernel<T, D, BN, true>), dim3((unsigned)total), dim3(NW * 64), 0, stream, args);
+  else
+    hipLaunchKernelGGL((fwd_pp_kernel<T, D, BN, false>), dim3((unsigned)total), dim3(NW * 64), 0, stream, args);
   return hipGetLastError();
 }
 

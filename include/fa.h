@@ -91,6 +91,20 @@ typedef struct {
   int32_t causal;       /* 0 or 1 */
   int32_t window_left;  /* -1 = unbounded, else >= 0 */
   int32_t window_right; /* -1 = unbounded, else >= 0 */
+  /* Score modifiers ([P4] section "进阶参数如何配置causal、window_size 与
+   * MQA/GQA": alibi_slopes, a positional bias that decays scores with
+   * distance; softcap, logits truncated to [-softcap, softcap]).  With
+   * x = scale * q_i . k_j and i' = i + seqlen_k - seqlen_q, the logit fed to
+   * the softmax is
+   *     min(max(x, -softcap), softcap) - slope(b, h) * |i' - j|
+   * (the clamp only when softcap > 0, the bias only when alibi_slopes is
+   * given), and the mask is applied after.  The backward differentiates
+   * this exactly: the clamp passes the gradient only where |x| < softcap. */
+  const float* alibi_slopes;  /* NULL, or float32 DEVICE array: slope(b, h) at
+                                 b * alibi_batch_stride + h, h < nheads_q */
+  int64_t alibi_batch_stride; /* >= 0; 0 = the same slopes for every batch entry */
+  float softcap;              /* 0 = off, else > 0 and finite */
+  int32_t reserved_mod;       /* 0 */
 } fa_params;
 
 /*

@@ -38,7 +38,9 @@ from .attention import (  # noqa: F401
     attention_fwd_rows,
     head_of,
     masked_softmax,
+    modified_logits,
     scores,
+    slope_of,
     visible,
 )
 from .kvcache import ALL_FUNCTIONS as _KVCACHE_FUNCTIONS

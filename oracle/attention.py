@@ -105,6 +105,39 @@ def masked_softmax(s, vis):
     return p, lse
 
 
+def slope_of(alibi_slopes, b, h):
+    """ALiBi slope of (batch b, query head h): alibi_slopes is None, (nheads_q,)
+    (the same for every batch entry) or (batch, nheads_q)."""
+    if alibi_slopes is None:
+        return None
+    a = np.asarray(alibi_slopes, dtype=np.float64)
+    return float(a[h] if a.ndim == 1 else a[b, h])
+
+
+def modified_logits(x, rows, seqlen_q, seqlen_k, slope=None, softcap=0.0):
+    """Score modifiers of [P4] section "进阶参数如何配置causal、window_size 与 MQA/GQA":
+    softcap truncates the logits to [-softcap, softcap]; alibi_slopes is a
+    positional bias that decays a score with the distance between query and key.
+
+    Readings (listed in DESIGN.md): the logits are the scaled scores x = scale * q.k;
+    the truncation is a clamp, applied first; the ALiBi bias is
+    -slope * |i' - j| with i' = i + seqlen_k - seqlen_q (the same alignment as
+    the mask), added after the clamp and before the mask.
+    Returns (logits, gate): gate is the derivative of the clamp, 1 where
+    |x| < softcap and 0 elsewhere (all ones without softcap).
+    """
+    out = x
+    gate = np.ones_like(x)
+    if softcap > 0:
+        out = np.clip(x, -softcap, softcap)
+        gate = (np.abs(x) < softcap).astype(np.float64)
+    if slope is not None:
+        aligned = np.asarray(rows, dtype=np.int64) - seqlen_q + seqlen_k
+        j = np.arange(seqlen_k, dtype=np.int64)
+        out = out - slope * np.abs(aligned[:, None] - j[None, :])
+    return out, gate
+
+
 def _check(q, k, v):
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be (batch, seqlen, nheads, headdim)")
@@ -121,12 +154,13 @@ def _row_blocks(nq, nk):
     return [(i, min(nq, i + r)) for i in range(0, nq, r)]
 
 
-def attention_fwd(q, k, v, causal=False, window=(-1, -1), scale=None):
+def attention_fwd(q, k, v, causal=False, window=(-1, -1), scale=None, alibi_slopes=None, softcap=0.0):
     """O = softmax(scale Q K^T + mask) V and the per-row log-sum-exp.
 
     [P4] section "长序列注意力为什么会爆内存" (the three steps), [P5] section
     "先搞清楚原理" (the standard_attention definition).  The whole score row is
-    materialised in float64 (row blocks only bound memory).
+    materialised in float64 (row blocks only bound memory).  Optional score
+    modifiers: :func:`modified_logits`.
     Returns (o, lse): o (B, Nq, Hq, d) and lse (B, Hq, Nq), both float64.
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
@@ -142,13 +176,15 @@ def attention_fwd(q, k, v, causal=False, window=(-1, -1), scale=None):
             for r0, r1 in _row_blocks(nq, nk):
                 rows = np.arange(r0, r1)
                 s = scores(q[b, r0:r1, h, :], kh, scale)
+                s, _ = modified_logits(s, rows, nq, nk, slope_of(alibi_slopes, b, h), softcap)
                 p, l_ = masked_softmax(s, visible(nq, nk, causal, window, rows))
                 o[b, r0:r1, h, :] = p @ vh
                 lse[b, h, r0:r1] = l_
     return o, lse
 
 
-def attention_fwd_rows(q, k, v, b, h, rows, causal=False, window=(-1, -1), scale=None):
+def attention_fwd_rows(q, k, v, b, h, rows, causal=False, window=(-1, -1), scale=None, alibi_slopes=None,
+                       softcap=0.0):
     """O and lse of selected query rows of one (batch, head): same definition as
     :func:`attention_fwd`, evaluated only where asked (for sampled checks at
     full size).  Returns (o_rows (R, d), lse_rows (R,))."""
@@ -159,11 +195,12 @@ def attention_fwd_rows(q, k, v, b, h, rows, causal=False, window=(-1, -1), scale
     rows = np.asarray(rows, dtype=np.int64)
     g = head_of(h, hq, hkv)
     s = scores(q[b, rows, h, :], k[b, :, g, :], scale)
+    s, _ = modified_logits(s, rows, nq, nk, slope_of(alibi_slopes, b, h), softcap)
     p, l_ = masked_softmax(s, visible(nq, nk, causal, window, rows))
     return p @ v[b, :, g, :], l_
 
 
-def attention_bwd(do, q, k, v, causal=False, window=(-1, -1), scale=None):
+def attention_bwd(do, q, k, v, causal=False, window=(-1, -1), scale=None, alibi_slopes=None, softcap=0.0):
     """Gradients of L = sum(O * dO) with respect to q, k and v.
 
     The pages state only that the backward pass recomputes the attention matrix
@@ -173,7 +210,9 @@ def attention_bwd(do, q, k, v, causal=False, window=(-1, -1), scale=None):
       dP = dO V^T,   D_i = sum_j P_ij dP_ij,   dS = P * (dP - D),
       dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO,
 
-    with dK and dV summed over the query heads that share a K/V head.
+    with dK and dV summed over the query heads that share a K/V head.  With the
+    score modifiers, P comes from the modified logits and dS is multiplied by
+    the clamp's derivative (the ALiBi bias does not depend on q or k).
     Returns (dq, dk, dv) in float64 with the shapes of q, k, v.
     """
     do, q, k, v = _as_f64(do), _as_f64(q), _as_f64(k), _as_f64(v)
@@ -193,15 +232,17 @@ def attention_bwd(do, q, k, v, causal=False, window=(-1, -1), scale=None):
                 rows = np.arange(r0, r1)
                 qr, dor = q[b, r0:r1, h, :], do[b, r0:r1, h, :]
                 s = scores(qr, kh, scale)
+                s, gate = modified_logits(s, rows, nq, nk, slope_of(alibi_slopes, b, h), softcap)
                 p, _ = masked_softmax(s, visible(nq, nk, causal, window, rows))
                 dp = dor @ vh.T
                 dsum = np.sum(p * dp, axis=1)
                 ds = p * (dp - dsum[:, None])
+                ds = ds * gate
                 dq[b, r0:r1, h, :] = scale * (ds @ kh)
                 dk[b, :, g, :] += scale * (ds.T @ qr)
                 dv[b, :, g, :] += p.T @ dor
     return dq, dk, dv
 
 
-ALL_FUNCTIONS = (head_of, visible, scores, masked_softmax, attention_fwd,
+ALL_FUNCTIONS = (head_of, visible, scores, masked_softmax, slope_of, modified_logits, attention_fwd,
                  attention_fwd_rows, attention_bwd)

@@ -32,12 +32,21 @@ import numpy as np
 from .attention import attention_fwd
 
 
+def _entry_slopes(alibi_slopes, b):
+    """Slopes of batch entry b as a (nheads_q,) array (None stays None)."""
+    if alibi_slopes is None:
+        return None
+    a = np.asarray(alibi_slopes, dtype=np.float64)
+    return a if a.ndim == 1 else a[b]
+
+
 def kvcache_fwd(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, causal=False, window=(-1, -1),
-                scale=None):
+                scale=None, alibi_slopes=None, softcap=0.0):
     """Append, then attend.
 
     q (B, Nq, Hq, d); k_cache, v_cache (B, capacity, Hkv, d); cache_seqlens (B,)
-    integers; k_new, v_new (B, Nq, Hkv, d) or both None.
+    integers; k_new, v_new (B, Nq, Hkv, d) or both None; alibi_slopes and softcap
+    as in :func:`oracle.attention.attention_fwd`.
     Returns (o (B, Nq, Hq, d), lse (B, Hq, Nq), k_cache_after, v_cache_after):
     o and lse in float64, the caches as copies in their input dtype.
     """
@@ -65,7 +74,7 @@ def kvcache_fwd(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, caus
         else:
             lk = length
         ob, lb = attention_fwd(q[b:b + 1], kc[b:b + 1, :lk], vc[b:b + 1, :lk], causal=causal, window=window,
-                               scale=scale)
+                               scale=scale, alibi_slopes=_entry_slopes(alibi_slopes, b), softcap=softcap)
         o[b] = ob[0]
         lse[b] = lb[0]
     return o, lse, kc, vc

@@ -34,27 +34,37 @@ def _ranges(cu_q, cu_k, total_q, total_k):
     return [(int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])) for b in range(cu_q.size - 1)]
 
 
-def attention_fwd_varlen(q, k, v, cu_q, cu_k, causal=False, window=(-1, -1), scale=None):
-    """Returns (o (total_q, Hq, d), lse (Hq, total_q)) in float64."""
+def _seq_slopes(alibi_slopes, b):
+    if alibi_slopes is None:
+        return None
+    a = np.asarray(alibi_slopes, dtype=np.float64)
+    return a if a.ndim == 1 else a[b]
+
+
+def attention_fwd_varlen(q, k, v, cu_q, cu_k, causal=False, window=(-1, -1), scale=None, alibi_slopes=None,
+                         softcap=0.0):
+    """Returns (o (total_q, Hq, d), lse (Hq, total_q)) in float64.  alibi_slopes is
+    (Hq,) or (batch, Hq), indexed by sequence."""
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
     total_q, hq, d = q.shape
     o = np.zeros(q.shape)
     lse = np.zeros((hq, total_q))
-    for q0, q1, k0, k1 in _ranges(cu_q, cu_k, total_q, k.shape[0]):
+    for b, (q0, q1, k0, k1) in enumerate(_ranges(cu_q, cu_k, total_q, k.shape[0])):
         ob, lb = attention_fwd(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], causal=causal, window=window,
-                               scale=scale)
+                               scale=scale, alibi_slopes=_seq_slopes(alibi_slopes, b), softcap=softcap)
         o[q0:q1] = ob[0]
         lse[:, q0:q1] = lb[0]
     return o, lse
 
 
-def attention_bwd_varlen(do, q, k, v, cu_q, cu_k, causal=False, window=(-1, -1), scale=None):
+def attention_bwd_varlen(do, q, k, v, cu_q, cu_k, causal=False, window=(-1, -1), scale=None, alibi_slopes=None,
+                         softcap=0.0):
     """Gradients (dq, dk, dv) of L = sum(O * dO) for every sequence, packed."""
     do, q, k, v = _as_f64(do), _as_f64(q), _as_f64(k), _as_f64(v)
     dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
-    for q0, q1, k0, k1 in _ranges(cu_q, cu_k, q.shape[0], k.shape[0]):
+    for b, (q0, q1, k0, k1) in enumerate(_ranges(cu_q, cu_k, q.shape[0], k.shape[0])):
         g = attention_bwd(do[None, q0:q1], q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], causal=causal,
-                          window=window, scale=scale)
+                          window=window, scale=scale, alibi_slopes=_seq_slopes(alibi_slopes, b), softcap=softcap)
         dq[q0:q1], dk[k0:k1], dv[k0:k1] = g[0][0], g[1][0], g[2][0]
     return dq, dk, dv
 

@@ -134,6 +134,11 @@ INVALID = [
     ("window below -1", dict(window_left=-2)),
     ("right window below -1", dict(window_right=-3)),
     ("causal not 0/1", dict(causal=2)),
+    ("negative softcap", dict(softcap=-1.0)),
+    ("nan softcap", dict(softcap=math.nan)),
+    ("inf softcap", dict(softcap=math.inf)),
+    ("negative alibi stride", dict(alibi_batch_stride=-1)),
+    ("reserved_mod set", dict(reserved_mod=1)),
 ]
 UNSUPPORTED = [
     ("bf16 headdim 96", dict(headdim=96, q_strides=(64 * 4 * 96, 4 * 96, 96), o_strides=(64 * 4 * 96, 4 * 96, 96),
@@ -144,6 +149,7 @@ UNSUPPORTED = [
     ("stride not 16 bytes", dict(k_strides=(64 * 2 * 64, 2 * 64, 68))),
     ("negative stride", dict(q_strides=(-16, 256, 64))),
     ("huge seqlen", dict(seqlen_q=1 << 31, seqlen_k=1 << 31)),
+    ("misaligned alibi slopes", dict(alibi_slopes=0x1002)),
 ]
 
 
@@ -275,7 +281,7 @@ def kv_params(num_splits=0, **kw):
     """B=2, Nq=1, Hq=4, Hkv=2, d=64, capacity 256, contiguous caches."""
     base = dict(seqlen_q=1, seqlen_k=256, q_strides=(1 * 4 * 64, 4 * 64, 64), o_strides=(1 * 4 * 64, 4 * 64, 64),
                 k_strides=(256 * 2 * 64, 2 * 64, 64), v_strides=(256 * 2 * 64, 2 * 64, 64))
-    base.update({k: v for k, v in kw.items() if not k.startswith(("knew", "vnew", "reserved"))})
+    base.update({k: v for k, v in kw.items() if not k.startswith(("knew", "vnew")) and k != "reserved"})
     p = N.FaKvParams()
     p.base = params(**base)
     p.knew_strides = N._I64x3(*kw.get("knew_strides", (1 * 2 * 64, 2 * 64, 64)))
@@ -445,3 +451,23 @@ def test_varlen_empty_problems_return_ok_without_device(lib):
 def test_varlen_valid_call_without_gpu_reports_hip_error(lib):
     assert call_fwd_vl(lib, vl_params()) == N.FA_ERR_HIP
     assert call_bwd_vl(lib, vl_params()) == N.FA_ERR_HIP
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-GPU error path")
+def test_valid_modifiers_pass_validation(lib):
+    # Slopes (aligned, per batch entry) and a softcap are accepted: the call
+    # gets as far as the device check.
+    p = params(alibi_slopes=0x1000, alibi_batch_stride=4, softcap=30.0)
+    assert call_fwd(lib, p) == N.FA_ERR_HIP
+    assert call_bwd(lib, p) == N.FA_ERR_HIP
+
+
+def test_python_binding_checks_slope_shape():
+    import torch
+    q = torch.zeros(2, 8, 4, 64, dtype=torch.bfloat16)
+    p = N.FaParams()
+    with pytest.raises(ValueError, match="alibi_slopes"):
+        N._set_modifiers(p, 4, 2, torch.zeros(3, dtype=torch.float32), 0.0)
+    with pytest.raises(ValueError, match="alibi_slopes"):
+        N._set_modifiers(p, 4, 2, torch.zeros(4, dtype=torch.float64), 0.0)
+    del q
