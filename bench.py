@@ -234,12 +234,42 @@ def decode_leg(calls):
     us = ev[0].elapsed_time(ev[1]) * 1e3 / calls
     nbytes = decode_bytes(w, lens.tolist())
     gbs = nbytes / (us * 1e-6) / 1e9
+
+    # The same call over a paged cache: 256-row pages in a shuffled pool,
+    # stored head-major inside each page (num_pages, Hkv, 256, d).
+    ps = 256
+    per = w.capacity // ps
+    n_pages = w.batch * per
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    table = torch.randperm(n_pages, generator=g).to(torch.int32).reshape(w.batch, per).to(dev)
+    kp = torch.empty((n_pages, w.nheads_kv, ps, w.headdim), dtype=q.dtype, device=dev)
+    vp = torch.empty_like(kp)
+    kpv, vpv = kp.permute(0, 2, 1, 3), vp.permute(0, 2, 1, 3)  # (num_pages, page_size, Hkv, d) views
+    for b in range(w.batch):
+        for p in range(per):
+            kpv[table[b, p]] = kc[b, p * ps:(p + 1) * ps]
+            vpv[table[b, p]] = vc[b, p * ps:(p + 1) * ps]
+
+    def call_paged():
+        fa.fwd_kvcache_paged(q, kpv, vpv, lens, table, kn, vn, out=out, lse=lse, workspace=ws, **kw)
+
+    for _ in range(10):
+        call_paged()
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(calls):
+        call_paged()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    us_paged = ev[0].elapsed_time(ev[1]) * 1e3 / calls
     return {
         "workload": w.name, "entry_point": "fa_fwd_kvcache",
         "config": {"batch": w.batch, "new_tokens": w.nq, "nheads_q": w.nheads_q, "nheads_kv": w.nheads_kv,
                    "headdim": w.headdim, "capacity": w.capacity, "cache_seqlens": lens.tolist(),
                    "cache_layout": w.kv_layout, "causal": w.causal, "num_splits": "auto"},
         "calls": calls, "us_per_call": round(us, 2),
+        "paged": {"page_size": ps, "layout": "shuffled page pool, head-major pages", "us_per_call": round(us_paged, 2),
+                  "achieved_GBps": round(nbytes / (us_paged * 1e-6) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes,
                      "timed": "whole call (split + merge kernels), events on the launch stream"},

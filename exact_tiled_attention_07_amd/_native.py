@@ -81,6 +81,8 @@ SIGNATURES = {
     "fa_bwd_varlen": (ctypes.c_int, [_PV, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "fa_fwd_kvcache_workspace_size": (ctypes.c_int, [_PK, ctypes.POINTER(ctypes.c_size_t)]),
     "fa_fwd_kvcache": (ctypes.c_int, [_PK, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
+    "fa_fwd_kvcache_paged": (ctypes.c_int, [_PK, ctypes.c_int32, ctypes.c_int64, _V, ctypes.c_int64, _V, _V, _V, _V,
+                                            _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_version": (ctypes.c_int, []),
@@ -430,6 +432,65 @@ def fwd_kvcache(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, *, c
         _check(lib.fa_fwd_kvcache(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
                                   _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), _ptr(workspace),
                                   workspace.numel(), _stream(q.device)))
+    return out, lse
+
+
+class _Layout:
+    """Shape, strides and dtype of a tensor view that is described, not built."""
+
+    def __init__(self, shape, strides, dtype):
+        self.shape, self._strides, self.dtype = torch.Size(shape), tuple(strides), dtype
+
+    def dim(self):
+        return len(self.shape)
+
+    def stride(self, i=None):
+        return self._strides if i is None else self._strides[i]
+
+
+def fwd_kvcache_paged(q, k_pages, v_pages, cache_seqlens, block_table, k_new=None, v_new=None, *, causal=False,
+                      window_size=(-1, -1), scale=None, num_splits=0, out=None, lse=None, workspace=None,
+                      alibi_slopes=None, softcap=0.0):
+    """fwd_kvcache over a paged cache: returns (o, lse).
+
+    k_pages, v_pages (num_pages, page_size, Hkv, d); block_table int32
+    (B, pages_per_entry) on the device: row j of entry b is row j % page_size
+    of page block_table[b, j // page_size].  The capacity of an entry is
+    pages_per_entry * page_size.
+    """
+    _require_gpu(q, k_pages, v_pages, cache_seqlens, block_table)
+    if k_new is not None:
+        _require_gpu(k_new, v_new)
+    lib = load_library()
+    if k_pages.dim() != 4 or k_pages.shape != v_pages.shape:
+        raise ValueError("k_pages and v_pages must be (num_pages, page_size, nheads_kv, headdim)")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != q.shape[0] \
+            or block_table.stride(1) != 1:
+        raise ValueError("block_table must be an int32 (batch, pages_per_entry) tensor with unit column stride")
+    if cache_seqlens.dtype != torch.int32 or tuple(cache_seqlens.shape) != (q.shape[0],) \
+            or not cache_seqlens.is_contiguous():
+        raise ValueError("cache_seqlens must be a contiguous int32 tensor of shape (batch,)")
+    num_pages, page_size = k_pages.shape[0], k_pages.shape[1]
+    cap = block_table.shape[1] * page_size
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    # Parameters as for a contiguous cache of the entries' capacity, with the
+    # pool's (page, row, head) strides in place of (batch, row, head).
+    shape = (q.shape[0], cap, k_pages.shape[2], k_pages.shape[3])
+    p = make_kv_params(q, _Layout(shape, k_pages.stride(), k_pages.dtype),
+                       _Layout(shape, v_pages.stride(), v_pages.dtype), out, k_new, v_new, causal=causal,
+                       window_size=window_size, scale=scale, num_splits=num_splits, alibi_slopes=alibi_slopes,
+                       softcap=softcap)
+    need = kvcache_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.fa_fwd_kvcache_paged(ctypes.byref(p), int(page_size), int(num_pages), _ptr(block_table),
+                                        block_table.stride(0), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                        _ptr(cache_seqlens), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse),
+                                        _ptr(workspace), workspace.numel(), _stream(q.device)))
     return out, lse
 
 

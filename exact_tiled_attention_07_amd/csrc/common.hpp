@@ -148,6 +148,12 @@ struct KvArgs {
   int64_t alibi_sb;
   float score_cap, inv_scale;
   int32_t mod;
+  // Paged caches (page_size 0: contiguous (B, cap, H, d) caches).  Row j of
+  // entry b is row j % page_size of page block_table[b * bt_sb + j / page_size]
+  // (clamped to [0, num_pages)); the caches' batch strides are page strides.
+  const int32_t* block_table;
+  int64_t bt_sb;
+  int32_t page_size, num_pages;
 };
 
 static constexpr float kLog2e = 1.4426950408889634f;

@@ -55,8 +55,14 @@ __device__ __forceinline__ void kv_append_chunk(const KvArgs& k, int64_t idx) {
   const char* src = static_cast<const char*>(which ? k.v_new : k.k_new) +
                     2 * (b * (which ? k.vn_sb : k.kn_sb) + (int64_t)i * (which ? k.vn_sn : k.kn_sn) +
                          h * (which ? k.vn_sh : k.kn_sh)) + 16 * c;
+  // Contiguous caches: entry b, row dst_row.  Paged: page of dst_row, row in it.
+  int64_t blk = b, row = dst_row;
+  if (k.page_size) {
+    blk = min(max(k.block_table[b * k.bt_sb + dst_row / k.page_size], 0), k.num_pages - 1);
+    row = dst_row % k.page_size;
+  }
   char* dst = static_cast<char*>(which ? k.v_cache : k.k_cache) +
-              2 * (b * (which ? k.vc_sb : k.kc_sb) + (int64_t)dst_row * (which ? k.vc_sn : k.kc_sn) +
+              2 * (blk * (which ? k.vc_sb : k.kc_sb) + row * (which ? k.vc_sn : k.kc_sn) +
                    h * (which ? k.vc_sh : k.kc_sh)) + 16 * c;
   *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
 }
@@ -97,7 +103,7 @@ struct KvStage {
   u32x4 vr[CPL];
 };
 
-template <class T, int D, int DEPTH, bool MOD>
+template <class T, int D, int DEPTH, bool MOD, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES))) void kv_split_kernel(KvArgs k) {
   constexpr int NST = D / 16;  // 16-wide d steps
   constexpr int CPL = KvStage<D>::CPL;
@@ -156,8 +162,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
     for (int st = 0; st < NST; ++st) qf[st] = u32x4{0u, 0u, 0u, 0u};
   }
 
-  const uint16_t* Kc = static_cast<const uint16_t*>(k.k_cache) + b * k.kc_sb + hk * k.kc_sh;
-  const uint16_t* Vc = static_cast<const uint16_t*>(k.v_cache) + b * k.vc_sb + hk * k.vc_sh;
+  // Cache base of this (entry, head); paged caches add the page of each tile.
+  const uint16_t* Kc = static_cast<const uint16_t*>(k.k_cache) + (PAGED ? 0 : b * k.kc_sb) + hk * k.kc_sh;
+  const uint16_t* Vc = static_cast<const uint16_t*>(k.v_cache) + (PAGED ? 0 : b * k.vc_sb) + hk * k.vc_sh;
   // Key j >= L is new row j - L (only when appending: otherwise Lk = L).
   const uint16_t* Kn = static_cast<const uint16_t*>(k.k_new) + b * k.kn_sb + hk * k.kn_sh;
   const uint16_t* Vn = static_cast<const uint16_t*>(k.v_new) + b * k.vn_sb + hk * k.vn_sh;
@@ -190,11 +197,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
   };
   // Rows past the end of the keys repeat the last one (their scores are masked).
   auto load_tile = [&](int t, KvStage<D>& st) {
+    if constexpr (PAGED) {
+      // The 32 rows of a tile lie in one page (page_size is a multiple of 32).
+      const int p = (32 * t) / k.page_size;
+      const int64_t pg = min(max(k.block_table[b * k.bt_sb + p], 0), k.num_pages - 1);
+      const int r0 = p * k.page_size;
+      const uint16_t* Kp = Kc + pg * k.kc_sb;
+      const uint16_t* Vp = Vc + pg * k.vc_sb;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int j = min(32 * t + crow[c], Lk - 1);
-      st.kr[c] = ld(krow(j) + 8 * ccol[c]);
-      st.vr[c] = ld(vrow(j) + 8 * ccol[c]);
+      for (int c = 0; c < CPL; ++c) {
+        const int j = min(32 * t + crow[c], Lk - 1);
+        st.kr[c] = ld((j < L ? Kp + (int64_t)(j - r0) * k.kc_sn : Kn + (int64_t)(j - L) * k.kn_sn) + 8 * ccol[c]);
+        st.vr[c] = ld((j < L ? Vp + (int64_t)(j - r0) * k.vc_sn : Vn + (int64_t)(j - L) * k.vn_sn) + 8 * ccol[c]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int j = min(32 * t + crow[c], Lk - 1);
+        st.kr[c] = ld(krow(j) + 8 * ccol[c]);
+        st.vr[c] = ld(vrow(j) + 8 * ccol[c]);
+      }
     }
   };
 
@@ -370,12 +392,18 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(KvArgs k) {
 
 template <class T, int D>
 static hipError_t launch_kv_t(const KvArgs& k, hipStream_t stream) {
-  if (k.mod)
-    hipLaunchKernelGGL((kv_split_kernel<T, D, FA_KV_DEPTH, true>), dim3((unsigned)(k.n_split + k.n_append)),
-                       dim3(64), 0, stream, k);
-  else
-    hipLaunchKernelGGL((kv_split_kernel<T, D, FA_KV_DEPTH, false>), dim3((unsigned)(k.n_split + k.n_append)),
-                       dim3(64), 0, stream, k);
+  const dim3 grid((unsigned)(k.n_split + k.n_append));
+  if (k.page_size) {
+    if (k.mod)
+      hipLaunchKernelGGL((kv_split_kernel<T, D, FA_KV_DEPTH, true, true>), grid, dim3(64), 0, stream, k);
+    else
+      hipLaunchKernelGGL((kv_split_kernel<T, D, FA_KV_DEPTH, false, true>), grid, dim3(64), 0, stream, k);
+  } else {
+    if (k.mod)
+      hipLaunchKernelGGL((kv_split_kernel<T, D, FA_KV_DEPTH, true, false>), grid, dim3(64), 0, stream, k);
+    else
+      hipLaunchKernelGGL((kv_split_kernel<T, D, FA_KV_DEPTH, false, false>), grid, dim3(64), 0, stream, k);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)k.B * k.Hq * k.Nq;

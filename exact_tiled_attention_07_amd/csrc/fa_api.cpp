@@ -469,12 +469,31 @@ fa_status fa_fwd_kvcache_workspace_size(const fa_kvcache_params* params, size_t*
   return FA_OK;
 }
 
-fa_status fa_fwd_kvcache(const fa_kvcache_params* params, const void* q, void* k_cache, void* v_cache,
-                         const int32_t* cache_seqlens, const void* k_new, const void* v_new, void* o, float* lse,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the contiguous and the paged entry points; page_size 0 means a
+// contiguous (batch, capacity, nheads_kv, headdim) cache.
+fa_status run_kvcache(const fa_kvcache_params* params, int32_t page_size, int64_t num_pages,
+                      const int32_t* block_table, int64_t block_table_stride, const void* q, void* k_cache,
+                      void* v_cache, const int32_t* cache_seqlens, const void* k_new, const void* v_new, void* o,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   fa_status s = check_kv_params(params);
   if (s != FA_OK) return s;
   const fa_params* p = &params->base;
+  if (page_size != 0) {
+    if (page_size < 0 || page_size % 32 != 0)
+      return fail(FA_ERR_INVALID_ARG, "page_size must be a positive multiple of 32 (got %d)", page_size);
+    if (p->seqlen_k % page_size != 0)
+      return fail(FA_ERR_INVALID_ARG, "the capacity (seqlen_k = %lld) must be a whole number of pages",
+                  (long long)p->seqlen_k);
+    if (num_pages < 1 || num_pages > INT32_MAX)
+      return fail(FA_ERR_INVALID_ARG, "num_pages must be in [1, 2^31 - 1] (got %lld)", (long long)num_pages);
+    if (block_table_stride < p->seqlen_k / page_size)
+      return fail(FA_ERR_INVALID_ARG, "block_table_stride (%lld) is below the pages per entry (%lld)",
+                  (long long)block_table_stride, (long long)(p->seqlen_k / page_size));
+  }
   if (p->headdim != 64 && p->headdim != 128)
     return fail(FA_ERR_UNSUPPORTED, "fa_fwd_kvcache needs headdim 64 or 128 (got %lld)", (long long)p->headdim);
   const bool nonempty = p->batch > 0 && p->seqlen_q > 0;
@@ -490,6 +509,11 @@ fa_status fa_fwd_kvcache(const fa_kvcache_params* params, const void* q, void* k
   if ((s = check_ptr(k_new, "k_new", k_new != nullptr)) != FA_OK) return s;
   if ((s = check_ptr(v_new, "v_new", v_new != nullptr)) != FA_OK) return s;
   if (!cache_seqlens) return fail(FA_ERR_INVALID_ARG, "cache_seqlens is NULL");
+  if (page_size != 0) {
+    if (!block_table) return fail(FA_ERR_INVALID_ARG, "block_table is NULL");
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
+      return fail(FA_ERR_UNSUPPORTED, "block_table is not 4-byte aligned");
+  }
   if ((reinterpret_cast<uintptr_t>(cache_seqlens) & 3u) != 0)
     return fail(FA_ERR_UNSUPPORTED, "cache_seqlens is not 4-byte aligned");
   const size_t need = kv_workspace_bytes(params);
@@ -539,9 +563,33 @@ fa_status fa_fwd_kvcache(const fa_kvcache_params* params, const void* q, void* k
   k.n_rb = (int32_t)n_rb;
   k.n_split = (int32_t)n_split;
   k.n_append = (int32_t)n_append;
+  k.block_table = block_table;
+  k.bt_sb = block_table_stride;
+  k.page_size = page_size;
+  k.num_pages = (int32_t)num_pages;
   const hipError_t e = fa::launch_kvcache(k, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kv-cache launch failed: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_kvcache(const fa_kvcache_params* params, const void* q, void* k_cache, void* v_cache,
+                         const int32_t* cache_seqlens, const void* k_new, const void* v_new, void* o, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return run_kvcache(params, 0, 0, nullptr, 0, q, k_cache, v_cache, cache_seqlens, k_new, v_new, o, lse, workspace,
+                     workspace_bytes, stream);
+}
+
+fa_status fa_fwd_kvcache_paged(const fa_kvcache_params* params, int32_t page_size, int64_t num_pages,
+                               const int32_t* block_table, int64_t block_table_stride, const void* q, void* k_cache,
+                               void* v_cache, const int32_t* cache_seqlens, const void* k_new, const void* v_new,
+                               void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (page_size == 0) return fail(FA_ERR_INVALID_ARG, "page_size must be a positive multiple of 32 (got 0)");
+  return run_kvcache(params, page_size, num_pages, block_table, block_table_stride, q, k_cache, v_cache,
+                     cache_seqlens, k_new, v_new, o, lse, workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_string(fa_status status) {

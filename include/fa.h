@@ -288,6 +288,30 @@ const char* fa_last_error(void);
 /* FA_VERSION of the built library. */
 int fa_version(void);
 
+/*
+ * Paged KV cache ([P4] section "增量解码场景flash_attn_with_kvcache": block_table
+ * turns on a cache stored in fixed-size blocks, which makes swapping and
+ * fragmentation easier to manage).  Everything is as in fa_fwd_kvcache except
+ * where the cache rows live:
+ *   k_cache, v_cache  pools of num_pages pages, (num_pages, page_size,
+ *                     nheads_kv, headdim); base.k_strides / v_strides are the
+ *                     (page, row, head) strides;
+ *   block_table       int32 DEVICE array: row j of batch entry b is row
+ *                     j % page_size of page block_table[b * block_table_stride
+ *                     + j / page_size].  Page numbers are read on the device and
+ *                     clamped to [0, num_pages), so a bad table gives wrong
+ *                     results but no access outside the pools;
+ *   base.seqlen_k     capacity of one entry, a whole number of pages
+ *                     (pages per entry = seqlen_k / page_size <= block_table_stride);
+ *   page_size         a positive multiple of 32 (a 32-key tile never spans pages).
+ * The append writes the new rows into the pages the table names.  Workspace:
+ * fa_fwd_kvcache_workspace_size.
+ */
+fa_status fa_fwd_kvcache_paged(const fa_kvcache_params* params, int32_t page_size, int64_t num_pages,
+                               const int32_t* block_table, int64_t block_table_stride, const void* q, void* k_cache,
+                               void* v_cache, const int32_t* cache_seqlens, const void* k_new, const void* v_new,
+                               void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Packed Q/K/V ([P4] section "上手 FlashAttention 的三步走": q, k and v stored
  * in one tensor) need no entry point of their own: a (batch, seqlen, 3, nheads,
  * headdim) tensor gives q, k and v as strided views (head stride headdim,

@@ -44,7 +44,7 @@ from .attention import (  # noqa: F401
     visible,
 )
 from .kvcache import ALL_FUNCTIONS as _KVCACHE_FUNCTIONS
-from .kvcache import kvcache_fwd  # noqa: F401
+from .kvcache import kvcache_fwd, kvcache_fwd_paged  # noqa: F401
 from .varlen import ALL_FUNCTIONS as _VARLEN_FUNCTIONS
 from .varlen import attention_bwd_varlen, attention_fwd_varlen  # noqa: F401
 

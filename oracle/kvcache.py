@@ -80,4 +80,32 @@ def kvcache_fwd(q, k_cache, v_cache, cache_seqlens, k_new=None, v_new=None, caus
     return o, lse, kc, vc
 
 
-ALL_FUNCTIONS = (kvcache_fwd,)
+def kvcache_fwd_paged(q, k_pages, v_pages, cache_seqlens, block_table, k_new=None, v_new=None, causal=False,
+                      window=(-1, -1), scale=None, alibi_slopes=None, softcap=0.0):
+    """The same computation over a paged cache ([P4] section "增量解码场景
+    flash_attn_with_kvcache": block_table turns on a cache stored in blocks).
+
+    k_pages, v_pages (num_pages, page_size, Hkv, d); block_table (B, pages per
+    entry) integers, clamped to [0, num_pages).  Reading: row j of entry b is
+    row j % page_size of page block_table[b, j // page_size]; the capacity of
+    an entry is its pages times page_size.  Steps: gather each entry's pages
+    into a contiguous cache, run :func:`kvcache_fwd`, write the pages back.
+    Returns (o, lse, k_pages_after, v_pages_after).
+    """
+    kp = np.array(k_pages, copy=True)
+    vp = np.array(v_pages, copy=True)
+    bt = np.clip(np.asarray(block_table, dtype=np.int64), 0, kp.shape[0] - 1)
+    nb, per = bt.shape
+    ps = kp.shape[1]
+    kc = np.stack([np.concatenate([kp[bt[b, p]] for p in range(per)]) for b in range(nb)])
+    vc = np.stack([np.concatenate([vp[bt[b, p]] for p in range(per)]) for b in range(nb)])
+    o, lse, kc, vc = kvcache_fwd(q, kc, vc, cache_seqlens, k_new, v_new, causal=causal, window=window, scale=scale,
+                                 alibi_slopes=alibi_slopes, softcap=softcap)
+    for b in range(nb):
+        for p in range(per):
+            kp[bt[b, p]] = kc[b, p * ps:(p + 1) * ps]
+            vp[bt[b, p]] = vc[b, p * ps:(p + 1) * ps]
+    return o, lse, kp, vp
+
+
+ALL_FUNCTIONS = (kvcache_fwd, kvcache_fwd_paged)

@@ -34,7 +34,7 @@ def header_functions():
 
 def test_header_declares_expected_entry_points():
     assert header_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd_kvcache",
+        ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd_kvcache", "fa_fwd_kvcache_paged",
          "fa_fwd_kvcache_workspace_size", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
          "fa_status_string", "fa_last_error", "fa_version"])
 
@@ -471,3 +471,35 @@ def test_python_binding_checks_slope_shape():
     with pytest.raises(ValueError, match="alibi_slopes"):
         N._set_modifiers(p, 4, 2, torch.zeros(4, dtype=torch.float64), 0.0)
     del q
+
+
+# --------------------------------------------------------------------------
+# fa_fwd_kvcache_paged: paging arguments.
+# --------------------------------------------------------------------------
+BT = 0x320000
+
+
+def call_paged(lib, p, page_size=64, num_pages=16, bt=BT, bt_stride=4, **kw):
+    a = dict(q=KQ, kc=KK, vc=KV_, lens=KS, kn=KN, vn=VN, o=KO, lse=KL, ws=KW, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.fa_fwd_kvcache_paged(ctypes.byref(p), page_size, num_pages, bt, bt_stride, a["q"], a["kc"], a["vc"],
+                                    a["lens"], a["kn"], a["vn"], a["o"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def test_paged_kvcache_validation(lib):
+    p = kv_params()  # capacity 256 = 4 pages of 64
+    for bad in (dict(page_size=0), dict(page_size=48), dict(page_size=-64), dict(page_size=512),
+                dict(num_pages=0), dict(bt_stride=3), dict(bt=None)):
+        assert call_paged(lib, p, **bad) == N.FA_ERR_INVALID_ARG, bad
+    assert call_paged(lib, p, bt=BT + 2) == N.FA_ERR_UNSUPPORTED
+    # the contiguous checks still apply
+    assert call_paged(lib, kv_params(num_splits=-1)) == N.FA_ERR_INVALID_ARG
+    assert call_paged(lib, p, lens=None) == N.FA_ERR_INVALID_ARG
+    assert call_paged(lib, kv_params(batch=0), q=None, kc=None, vc=None, lens=None, kn=None, vn=None, o=None,
+                      lse=None, ws=None, ws_bytes=0) == N.FA_OK
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-GPU error path")
+def test_paged_kvcache_valid_call_without_gpu_reports_hip_error(lib):
+    assert call_paged(lib, kv_params()) == N.FA_ERR_HIP
+    assert call_paged(lib, kv_params(), page_size=256, bt_stride=1) == N.FA_ERR_HIP

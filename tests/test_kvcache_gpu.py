@@ -273,3 +273,68 @@ def test_decode_workload_full_size(name):
     for b in range(w.batch):
         mask[b, int(lens[b]):int(lens[b]) + w.nq] = False
     assert torch.equal(kcd.cpu()[mask], kc[mask]) and torch.equal(vcd.cpu()[mask], vc[mask])
+
+
+# ---------------------------------------------------------------------------
+# Paged caches (fa_fwd_kvcache_paged).
+# ---------------------------------------------------------------------------
+def _paged_from(kc, vc, ps, rng, spare=3):
+    """Scatter contiguous (B, cap, H, d) caches into a shuffled page pool with
+    spare pages; returns (k_pages, v_pages, table)."""
+    nb, cap = kc.shape[:2]
+    per = cap // ps
+    n_pages = nb * per + spare
+    perm = torch.from_numpy(rng.permutation(n_pages)).long()
+    table = perm[:nb * per].reshape(nb, per).to(torch.int32)
+    g = torch.Generator("cpu").manual_seed(int(rng.integers(1 << 31)))
+    kp = torch.randn((n_pages, ps) + tuple(kc.shape[2:]), generator=g).to(kc.dtype)
+    vp = torch.randn((n_pages, ps) + tuple(kc.shape[2:]), generator=g).to(kc.dtype)
+    for b in range(nb):
+        for p in range(per):
+            kp[table[b, p]] = kc[b, p * ps:(p + 1) * ps]
+            vp[table[b, p]] = vc[b, p * ps:(p + 1) * ps]
+    return kp, vp, table
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
+@pytest.mark.parametrize("ps", [32, 64, 256])
+@pytest.mark.parametrize("mask", [dict(causal=True), dict(window_size=(40, 0)), dict()], ids=["causal", "w40", "full"])
+def test_paged_matches_oracle(dtype, d, ps, mask):
+    rng = np.random.default_rng(ps + d)
+    for append in (True, False):
+        b, nq, hq, hkv, cap = 3, 2, 8, 2, 4 * 256
+        q, kc, vc, kn, vn = _draw(b, nq, hq, hkv, d, cap, dtype, seed=900 + ps)
+        lens = [cap - 1, 37, 600]  # the first entry overflows when appending
+        kp, vp, table = _paged_from(kc, vc, ps, rng)
+        _note(f"paged {dtype} d={d} ps={ps} {mask} append={append}")
+        kpd, vpd = kp.cuda(), vp.cuda()
+        o, lse = fa.fwd_kvcache_paged(q.cuda(), kpd, vpd, torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                                      table.cuda(), kn.cuda() if append else None, vn.cuda() if append else None,
+                                      **mask)
+        torch.cuda.synchronize()
+        o_ref, lse_ref, kp_ref, vp_ref = oracle.kvcache_fwd_paged(
+            f64(q), f64(kp), f64(vp), np.array(lens), table.numpy(), f64(kn) if append else None,
+            f64(vn) if append else None, causal=mask.get("causal", False),
+            window=tuple(mask.get("window_size", (-1, -1))))
+        assert_close(o, o_ref, TOL[q.dtype], "O")
+        assert_close(lse, lse_ref, TOL[q.dtype], "LSE")
+        assert np.array_equal(f64(kpd), kp_ref) and np.array_equal(f64(vpd), vp_ref), "pages after the append"
+
+
+def test_paged_equals_contiguous_bitwise_full_size():
+    # The benchmark's decode workload with its cache cut into 256-row pages in
+    # a shuffled pool: the same tiles in the same order, so the same bits.
+    w = DECODE_WORKLOADS["bf16_decode_b8_hq32_hkv8_d128_cap16384"]
+    q, kc, vc, kn, vn, lens = make_decode_inputs(w)
+    kp, vp, table = _paged_from(kc.contiguous(), vc.contiguous(), 256, np.random.default_rng(5))
+    qd, knd, vnd, lensd = q.cuda(), kn.cuda(), vn.cuda(), lens.cuda()
+    kcd, vcd = kc.cuda(), vc.cuda()
+    o1, l1 = fa.fwd_kvcache(qd, kcd, vcd, lensd, knd, vnd, causal=True)
+    kpd, vpd = kp.cuda(), vp.cuda()
+    o2, l2 = fa.fwd_kvcache_paged(qd, kpd, vpd, lensd, table.cuda(), knd, vnd, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for b in range(w.batch):
+        r = int(lens[b])
+        assert torch.equal(kpd[int(table[b, r // 256]), r % 256].cpu(), kn[b, 0])
+        assert torch.equal(vpd[int(table[b, r // 256]), r % 256].cpu(), vn[b, 0])

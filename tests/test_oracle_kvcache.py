@@ -240,3 +240,58 @@ def test_planted_mistake_is_caught(name, old, new):
     except (ValueError, IndexError):
         ok = False
     assert not ok, f"planted mistake '{name}' was not caught by the pins"
+
+
+# --------------------------------------------------------------------------
+# Paged caches.
+# --------------------------------------------------------------------------
+def _pages_of(kc, ps):
+    """Contiguous (B, cap, H, d) cache -> pages (B * cap / ps, ps, H, d), identity table."""
+    nb, cap = kc.shape[:2]
+    pages = kc.reshape(nb * (cap // ps), ps, *kc.shape[2:])
+    return pages, np.arange(nb * (cap // ps)).reshape(nb, cap // ps)
+
+
+def test_paged_with_identity_table_equals_contiguous():
+    rng = np.random.default_rng(21)
+    q = _rand((2, 3, 4, 3), rng)
+    kc, vc = _rand((2, 8, 2, 3), rng), _rand((2, 8, 2, 3), rng)
+    kn, vn = _rand((2, 3, 2, 3), rng), _rand((2, 3, 2, 3), rng)
+    lens = np.array([2, 6])
+    o, lse, kc1, vc1 = oracle.kvcache_fwd(q, kc, vc, lens, kn, vn, causal=True)
+    kp, bt = _pages_of(kc, 4)
+    vp, _ = _pages_of(vc, 4)
+    o2, lse2, kp1, vp1 = oracle.kvcache_fwd_paged(q, kp, vp, lens, bt, kn, vn, causal=True)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    assert np.array_equal(kp1.reshape(kc1.shape), kc1) and np.array_equal(vp1.reshape(vc1.shape), vc1)
+
+
+def test_paged_table_order_and_append_placement():
+    # Scattering the pages through a permuted table changes nothing but where
+    # the rows live; the appended rows land in the pages the table names and
+    # no other page changes.
+    rng = np.random.default_rng(22)
+    nb, per, ps, h, d = 3, 3, 4, 1, 2
+    q = _rand((nb, 2, 2, d), rng)
+    kc, vc = _rand((nb, per * ps, h, d), rng), _rand((nb, per * ps, h, d), rng)
+    kn, vn = _rand((nb, 2, h, d), rng), _rand((nb, 2, h, d), rng)
+    lens = np.array([3, 7, 10])
+    o, lse, kc1, _ = oracle.kvcache_fwd(q, kc, vc, lens, kn, vn, causal=True, window=(2, -1))
+    perm = rng.permutation(nb * per + 2)          # two spare pages
+    bt = perm[:nb * per].reshape(nb, per)
+    kp = _rand((nb * per + 2, ps, h, d), rng)
+    vp = _rand((nb * per + 2, ps, h, d), rng)
+    for b in range(nb):
+        for p in range(per):
+            kp[bt[b, p]] = kc[b, p * ps:(p + 1) * ps]
+            vp[bt[b, p]] = vc[b, p * ps:(p + 1) * ps]
+    o2, lse2, kp1, _ = oracle.kvcache_fwd_paged(q, kp, vp, lens, bt, kn, vn, causal=True, window=(2, -1))
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    for b in range(nb):
+        for r in range(lens[b], lens[b] + 2):
+            assert np.array_equal(kp1[bt[b, r // ps], r % ps], kn[b, r - lens[b]])
+    spare = perm[nb * per:]
+    assert np.array_equal(kp1[spare], kp[spare])
+    changed = {(int(bt[b, r // ps])) for b in range(nb) for r in range(lens[b], lens[b] + 2)}
+    for pg in set(range(nb * per)) - changed:
+        assert np.array_equal(kp1[pg], kp[pg])
