@@ -89,8 +89,8 @@ def flops(w):
 # built from the sources whose SHA-256 is recorded here and are reported as
 # null for any other source.
 DKDV_TRAFFIC = {
-    "sources_sha256": "1423a15eeb58e31bf3d1d4d36d80ad5a2cd7e095ee345cf22409d1b81c1d4988",
-    "bytes_per_launch": 2261461327,
+    "sources_sha256": "7dd81866cd5d55f3de3c5da8ec733d9fd88ae83fe6fc8a210d1a7fd83ecb8525",
+    "bytes_per_launch": 2252646893,
 }
 
 
