@@ -387,12 +387,12 @@ struct DkdvWs {
     const uint16_t* Kp = static_cast<const uint16_t*>(a->k) + b * a->k_sb + hk * a->k_sh;
     const uint16_t* Vp = static_cast<const uint16_t*>(a->v) + b * a->v_sb + hk * a->v_sh;
     if (key < a->Nk) {
-      const uint16_t* kr = Kp + (int64_t)key * a->k_sn + 8 * hf;
-      const uint16_t* vr = Vp + (int64_t)key * a->v_sn + 8 * hf;
+      const uint16_t* kr = Kp + (int64_t)key * a->k_sn;
+      const uint16_t* vr = Vp + (int64_t)key * a->v_sn;
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        kf[st] = *reinterpret_cast<const u32x4*>(kr + 16 * st);
-        vf[st] = *reinterpret_cast<const u32x4*>(vr + 16 * st);
+        kf[st] = load_cols(kr, 16 * st + 8 * hf, a->D);
+        vf[st] = load_cols(vr, 16 * st + 8 * hf, a->D);
       }
     } else {
 #pragma unroll
@@ -453,8 +453,8 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
   x.n_qt = (i_hi >= i_lo) ? i_hi / BMQ - x.qt_lo + 1 : 0;
   x.n_items = x.n_qt * a.G;  // (query tile, query head of the group) pairs
   x.off.init(lane);
-  x.qd.init(x.kb, lane, a.q_sn);
-  x.dd.init(x.kb, lane, a.o_sn);
+  x.qd.init(x.kb, lane, a.q_sn, a.D / 8);
+  x.dd.init(x.kb, lane, a.o_sn, a.D / 8);
 
   if (x.n_items > 0 && wave < L::KW) {
     x.issue(typename DkdvWs<T, D, BMQ, MOD>::Cursor{0, 0}, 0);
@@ -479,6 +479,7 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * db + 8 * g4 + 4 * hf;
+        if (d0 >= a.D) continue;
         *reinterpret_cast<u32x2*>(dkp + d0) =
             u32x2{T::pack(dka[db][4 * g4] * sc, dka[db][4 * g4 + 1] * sc),
                   T::pack(dka[db][4 * g4 + 2] * sc, dka[db][4 * g4 + 3] * sc)};
@@ -639,12 +640,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
   x.lse2 = INFINITY;
   x.dsum = 0.f;
   if (qrow < a.Nq) {
-    const uint16_t* qr = Qp + (int64_t)qrow * a.q_sn + 8 * hf;
-    const uint16_t* dr = dOp + (int64_t)qrow * a.o_sn + 8 * hf;
+    const uint16_t* qr = Qp + (int64_t)qrow * a.q_sn;
+    const uint16_t* dr = dOp + (int64_t)qrow * a.o_sn;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-      x.qf[st] = *reinterpret_cast<const u32x4*>(qr + 16 * st);
-      x.df[st] = *reinterpret_cast<const u32x4*>(dr + 16 * st);
+      x.qf[st] = load_cols(qr, 16 * st + 8 * hf, a.D);
+      x.df[st] = load_cols(dr, 16 * st + 8 * hf, a.D);
     }
     const int64_t ri = b * a.ws_sb + hq * a.ws_sh + qrow;
     x.lse2 = a.lse2[ri];
@@ -665,8 +666,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) x.dqa[db] = f32x16{};
   x.off.init(lane);
-  x.kd.init(wave, lane, a.k_sn);
-  x.vd.init(wave, lane, a.v_sn);
+  x.kd.init(wave, lane, a.k_sn, a.D / 8);
+  x.vd.init(wave, lane, a.v_sn, a.D / 8);
 
   if (t_lo <= x.t_hi) {
     x.kd.issue(x.Kp, a.k_sn, t_lo * BN, a.Nk, smem, wave);
@@ -689,6 +690,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * db + 8 * g4 + 4 * hf;
+        if (d0 >= a.D) continue;
         *reinterpret_cast<u32x2*>(dqp + d0) =
             u32x2{T::pack(x.dqa[db][4 * g4] * sc, x.dqa[db][4 * g4 + 1] * sc),
                   T::pack(x.dqa[db][4 * g4 + 2] * sc, x.dqa[db][4 * g4 + 3] * sc)};
@@ -734,12 +736,13 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream, int stages
 }
 
 hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t stream, int stages) {
+  // Head dims below 64 / 128 run the 64 / 128 kernels with the rest masked.
   if (a.dtype == kBF16) {
-    if (a.D == 128) return launch_bwd_t<BF16, 128>(a, stream, stages);
-    if (a.D == 64) return launch_bwd_t<BF16, 64>(a, stream, stages);
+    if (a.D > 64 && a.D <= 128) return launch_bwd_t<BF16, 128>(a, stream, stages);
+    if (a.D >= 8 && a.D <= 64) return launch_bwd_t<BF16, 64>(a, stream, stages);
   } else if (a.dtype == kF16) {
-    if (a.D == 128) return launch_bwd_t<F16, 128>(a, stream, stages);
-    if (a.D == 64) return launch_bwd_t<F16, 64>(a, stream, stages);
+    if (a.D > 64 && a.D <= 128) return launch_bwd_t<F16, 128>(a, stream, stages);
+    if (a.D >= 8 && a.D <= 64) return launch_bwd_t<F16, 64>(a, stream, stages);
   }
   return hipErrorInvalidValue;
 }

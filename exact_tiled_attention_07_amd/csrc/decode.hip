@@ -154,9 +154,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
   // Q rows as B operands: lane holds d = 16*st + 8*hf + (0..7) of its row.
   u32x4 qf[NST];
   if (valid) {
-    const uint16_t* qr = static_cast<const uint16_t*>(k.q) + b * k.q_sb + (int64_t)i * k.q_sn + hq * k.q_sh + 8 * hf;
+    const uint16_t* qr = static_cast<const uint16_t*>(k.q) + b * k.q_sb + (int64_t)i * k.q_sn + hq * k.q_sh;
 #pragma unroll
-    for (int st = 0; st < NST; ++st) qf[st] = *reinterpret_cast<const u32x4*>(qr + 16 * st);
+    for (int st = 0; st < NST; ++st) qf[st] = load_cols(qr, 16 * st + 8 * hf, k.D);
   } else {
 #pragma unroll
     for (int st = 0; st < NST; ++st) qf[st] = u32x4{0u, 0u, 0u, 0u};
@@ -192,6 +192,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
 
   // Every K/V element is read once: the non-temporal hint keeps the stream
   // from displacing reusable lines (measured 10% faster on MI355X).
+  // A lane's column chunk is the same in every row it loads (64 is a multiple
+  // of D / 8).  With a head dim below D, a lane whose chunk lies past it loads
+  // chunk 0 of the same row instead (valid memory, no select): that copy only
+  // meets the zero columns of Q in S and lands in O columns that are never
+  // stored.
+  static_assert(64 % (D / 8) == 0, "one column chunk per lane");
+  const int cload = (lane % (D / 8)) < k.D / 8 ? lane % (D / 8) : 0;
   auto ld = [](const uint16_t* p) -> u32x4 {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   };
@@ -207,15 +214,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const int j = min(32 * t + crow[c], Lk - 1);
-        st.kr[c] = ld((j < L ? Kp + (int64_t)(j - r0) * k.kc_sn : Kn + (int64_t)(j - L) * k.kn_sn) + 8 * ccol[c]);
-        st.vr[c] = ld((j < L ? Vp + (int64_t)(j - r0) * k.vc_sn : Vn + (int64_t)(j - L) * k.vn_sn) + 8 * ccol[c]);
+        st.kr[c] = ld((j < L ? Kp + (int64_t)(j - r0) * k.kc_sn : Kn + (int64_t)(j - L) * k.kn_sn) + 8 * cload);
+        st.vr[c] = ld((j < L ? Vp + (int64_t)(j - r0) * k.vc_sn : Vn + (int64_t)(j - L) * k.vn_sn) + 8 * cload);
       }
     } else {
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const int j = min(32 * t + crow[c], Lk - 1);
-        st.kr[c] = ld(krow(j) + 8 * ccol[c]);
-        st.vr[c] = ld(vrow(j) + 8 * ccol[c]);
+        st.kr[c] = ld(krow(j) + 8 * cload);
+        st.vr[c] = ld(vrow(j) + 8 * cload);
       }
     }
   };
@@ -383,7 +390,7 @@ __global__ __launch_bounds__(256) void kv_merge_kernel(KvArgs k) {
   const int64_t bh = row / k.Nq;
   const int hq = (int)(bh % k.Hq);
   const int b = (int)(bh / k.Hq);
-  if (ps == 0) {
+  if (ps == 0 && 4 * cg < k.D) {
     uint16_t* op = static_cast<uint16_t*>(k.o) + b * k.o_sb + (int64_t)i * k.o_sn + hq * k.o_sh + 4 * cg;
     *reinterpret_cast<u32x2*>(op) = u32x2{T::pack(acc[0] * inv, acc[1] * inv), T::pack(acc[2] * inv, acc[3] * inv)};
   }
@@ -412,12 +419,13 @@ static hipError_t launch_kv_t(const KvArgs& k, hipStream_t stream) {
 }
 
 hipError_t launch_kvcache(const KvArgs& k, hipStream_t stream) {
+  // Head dims below 64 / 128 run the 64 / 128 kernels with the rest masked.
   if (k.dtype == kBF16) {
-    if (k.D == 128) return launch_kv_t<BF16, 128>(k, stream);
-    if (k.D == 64) return launch_kv_t<BF16, 64>(k, stream);
+    if (k.D > 64 && k.D <= 128) return launch_kv_t<BF16, 128>(k, stream);
+    if (k.D >= 8 && k.D <= 64) return launch_kv_t<BF16, 64>(k, stream);
   } else if (k.dtype == kF16) {
-    if (k.D == 128) return launch_kv_t<F16, 128>(k, stream);
-    if (k.D == 64) return launch_kv_t<F16, 64>(k, stream);
+    if (k.D > 64 && k.D <= 128) return launch_kv_t<F16, 128>(k, stream);
+    if (k.D >= 8 && k.D <= 64) return launch_kv_t<F16, 64>(k, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -75,8 +75,9 @@ fa_status check_params(const fa_params* p) {
     if (p->headdim > 128 || p->headdim % 4 != 0)
       return fail(FA_ERR_UNSUPPORTED, "fp32 headdim must be a multiple of 4 in [4, 128] (got %lld)",
                   (long long)p->headdim);
-  } else if (p->headdim != 64 && p->headdim != 128) {
-    return fail(FA_ERR_UNSUPPORTED, "fp16/bf16 headdim must be 64 or 128 (got %lld)", (long long)p->headdim);
+  } else if (p->headdim > 128 || p->headdim % 8 != 0) {
+    return fail(FA_ERR_UNSUPPORTED, "fp16/bf16 headdim must be a multiple of 8 in [8, 128] (got %lld)",
+                (long long)p->headdim);
   }
   // Kernels address a tile of up to 128 rows with 32-bit byte offsets.
   if (p->q_strides[1] > (int64_t(1) << 22) || p->k_strides[1] > (int64_t(1) << 22) ||
@@ -220,10 +221,13 @@ int64_t kv_parts(const fa_kvcache_params* kp) {
   return std::max<int64_t>(1, std::min<int64_t>({s, tiles, kMaxKvParts}));
 }
 
+// Head dim of the kernels that run a head dim (64 or 128; smaller ones are masked).
+int64_t kernel_headdim(int64_t d) { return d <= 64 ? 64 : 128; }
+
 size_t kv_workspace_bytes(const fa_kvcache_params* kp) {
   const fa_params* p = &kp->base;
   const size_t rows = (size_t)p->batch * (size_t)p->nheads_q * (size_t)p->seqlen_q;
-  const size_t n = rows * (size_t)kv_parts(kp) * (size_t)(p->headdim + 1) * sizeof(float);
+  const size_t n = rows * (size_t)kv_parts(kp) * (size_t)(kernel_headdim(p->headdim) + 1) * sizeof(float);
   return ((n + 255) / 256) * 256;
 }
 
@@ -494,8 +498,7 @@ fa_status run_kvcache(const fa_kvcache_params* params, int32_t page_size, int64_
       return fail(FA_ERR_INVALID_ARG, "block_table_stride (%lld) is below the pages per entry (%lld)",
                   (long long)block_table_stride, (long long)(p->seqlen_k / page_size));
   }
-  if (p->headdim != 64 && p->headdim != 128)
-    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_kvcache needs headdim 64 or 128 (got %lld)", (long long)p->headdim);
+
   const bool nonempty = p->batch > 0 && p->seqlen_q > 0;
   if (!nonempty) return FA_OK;
   if ((k_new == nullptr) != (v_new == nullptr))
@@ -540,7 +543,7 @@ fa_status run_kvcache(const fa_kvcache_params* params, int32_t page_size, int64_
   k.o = o; k.lse = lse; k.cache_seqlens = cache_seqlens;
   const size_t rows = (size_t)p->batch * (size_t)p->nheads_q * (size_t)p->seqlen_q;
   k.ws_o = static_cast<float*>(workspace);
-  k.ws_lse = k.ws_o + rows * (size_t)S * (size_t)p->headdim;
+  k.ws_lse = k.ws_o + rows * (size_t)S * (size_t)kernel_headdim(p->headdim);
   k.q_sb = p->q_strides[0]; k.q_sn = p->q_strides[1]; k.q_sh = p->q_strides[2];
   k.kc_sb = p->k_strides[0]; k.kc_sn = p->k_strides[1]; k.kc_sh = p->k_strides[2];
   k.vc_sb = p->v_strides[0]; k.vc_sn = p->v_strides[1]; k.vc_sh = p->v_strides[2];

@@ -242,11 +242,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const uint16_t* Qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh;
 
-  // Q as the B operand of S^T = K Q^T: lane holds d = 16*st + 8*hf + (0..7).
+  // Q as the B operand of S^T = K Q^T: lane holds d = 16*st + 8*hf + (0..7)
+  // (zeros past a head dim below D).
   if (qrow < a.Nq) {
-    const uint16_t* qr = Qp + (int64_t)qrow * a.q_sn + 8 * hf;
+    const uint16_t* qr = Qp + (int64_t)qrow * a.q_sn;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) x.qf[st] = *reinterpret_cast<const u32x4*>(qr + 16 * st);
+    for (int st = 0; st < D / 16; ++st) x.qf[st] = load_cols(qr, 16 * st + 8 * hf, a.D);
   } else {
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) x.qf[st] = u32x4{0u, 0u, 0u, 0u};
@@ -288,8 +289,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = 0; i < TILE * 2 / (512 * 16); ++i)
     reinterpret_cast<u32x4*>(vbuf + TILE)[i * 512 + tid] = u32x4{0u, 0u, 0u, 0u};
 
-  x.kd.init(wave, lane, a.k_sn);
-  x.vd.init(wave, lane, a.v_sn);
+  x.kd.init(wave, lane, a.k_sn, a.D / 8);
+  x.vd.init(wave, lane, a.v_sn, a.D / 8);
   if (group_a && x.n > 0) {
     x.kd.issue(x.Kp, a.k_sn, x.t_lo * BN, a.Nk, kbuf, wave);
     wait_all_loads();
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int d0 = 32 * db + 8 * g4 + 4 * hf;
         const u32x2 w{T::pack(x.oacc[db][4 * g4] * inv, x.oacc[db][4 * g4 + 1] * inv),
                       T::pack(x.oacc[db][4 * g4 + 2] * inv, x.oacc[db][4 * g4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + d0) = w;
+        if (d0 < a.D) *reinterpret_cast<u32x2*>(op + d0) = w;
       }
     }
     if (hf == 0)
@@ -376,12 +377,13 @@ static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t stream) {
+  // Head dims below 64 / 128 run the 64 / 128 kernels with the rest masked.
   if (a.dtype == kBF16) {
-    if (a.D == 128) return launch_fwd_t<BF16, 128, FA_FWD_BN, 8>(a, stream);
-    if (a.D == 64) return launch_fwd_t<BF16, 64, FA_FWD_BN, 8>(a, stream);
+    if (a.D > 64 && a.D <= 128) return launch_fwd_t<BF16, 128, FA_FWD_BN, 8>(a, stream);
+    if (a.D >= 8 && a.D <= 64) return launch_fwd_t<BF16, 64, FA_FWD_BN, 8>(a, stream);
   } else if (a.dtype == kF16) {
-    if (a.D == 128) return launch_fwd_t<F16, 128, FA_FWD_BN, 8>(a, stream);
-    if (a.D == 64) return launch_fwd_t<F16, 64, FA_FWD_BN, 8>(a, stream);
+    if (a.D > 64 && a.D <= 128) return launch_fwd_t<F16, 128, FA_FWD_BN, 8>(a, stream);
+    if (a.D >= 8 && a.D <= 64) return launch_fwd_t<F16, 64, FA_FWD_BN, 8>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -84,6 +84,12 @@ struct SwzOffsets {
   }
 };
 
+// 16 bytes at element offset col of a row, or zeros where col lies past the
+// row's head dim dh (head dims are multiples of 8, so a chunk is all in or all out).
+__device__ __forceinline__ u32x4 load_cols(const uint16_t* row, int col, int dh) {
+  return col < dh ? *reinterpret_cast<const u32x4*>(row + col) : u32x4{0u, 0u, 0u, 0u};
+}
+
 // ===========================================================================
 // Direct global -> LDS tile loads (global_load_lds_dwordx4).
 //
@@ -112,17 +118,22 @@ struct DmaTile {
   static constexpr int PER_WAVE = (NBLK + NW - 1) / NW;
   static_assert(ROWS % RPB == 0, "tile rows must fill whole 1 KB blocks");
   uint32_t off[PER_WAVE];  // byte offsets of this lane's chunk in each of its blocks
-  int lane_row, lane_pc;
+  int lane_row, lane_pc, dch;
 
-  __device__ __forceinline__ void init(int wave, int lane, int64_t row_stride_elems) {
+  // dch = 16-byte chunks of a row that hold data (head dim / 8, <= D / 8).  A
+  // lane whose chunk lies past it loads chunk 0 of the same row instead (valid
+  // memory, no per-load test): the kernels pair those LDS columns only with
+  // zero register columns or with outputs that are never stored.
+  __device__ __forceinline__ void init(int wave, int lane, int64_t row_stride_elems, int dch_ = D / 8) {
     lane_row = lane / CPR;
     lane_pc = lane % CPR;
+    dch = dch_;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int j = wave + i * NW;
       const int r = j * RPB + lane_row;
       const int c = lane_pc ^ Swz<D>::sw(r);
-      off[i] = (uint32_t)(r * row_stride_elems * 2 + c * 16);
+      off[i] = (uint32_t)(r * row_stride_elems * 2 + (c < dch ? c : 0) * 16);
     }
   }
   // Rows row0 .. row0+ROWS-1 of a tensor whose rows start every row_stride
@@ -144,7 +155,8 @@ struct DmaTile {
         if (NBLK % NW == 0 || j < NBLK) {
           const int r = j * RPB + lane_row;
           const int row = min(row0 + r, nrows - 1);
-          const int c = lane_pc ^ Swz<D>::sw(r);
+          int c = lane_pc ^ Swz<D>::sw(r);
+          c = c < dch ? c : 0;
           dma16(reinterpret_cast<const char*>(base + (int64_t)row * row_stride) + c * 16, lds_tile + j * 512);
         }
       }

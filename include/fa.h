@@ -81,7 +81,7 @@ typedef struct {
   int64_t batch;
   int64_t seqlen_q, seqlen_k;
   int64_t nheads_q, nheads_kv; /* nheads_q must be a multiple of nheads_kv */
-  int64_t headdim;             /* fp16/bf16: 64 or 128; fp32: multiple of 4, 4..128 */
+  int64_t headdim;             /* fp16/bf16: multiple of 8, 8..128; fp32: multiple of 4, 4..128 */
   /* (batch, seq, head) strides in elements; the headdim axis has stride 1.
    * In fa_bwd, dout uses o_strides, dq uses q_strides, dk uses k_strides and
    * dv uses v_strides. */
@@ -233,7 +233,7 @@ fa_status fa_bwd_varlen(const fa_varlen_params* params, const void* dout, const 
  * fill the GPU).
  *
  * base: batch; seqlen_q = Nq new queries per batch entry; seqlen_k = cache
- *   capacity in rows; nheads_q, nheads_kv, headdim (64 or 128); q_strides and
+ *   capacity in rows; nheads_q, nheads_kv, headdim (multiple of 8, <= 128); q_strides and
  *   o_strides for q and o (batch, Nq, nheads_q, headdim); k_strides and
  *   v_strides for the caches (batch, capacity, nheads_kv, headdim); dtype
  *   FA_F16 or FA_BF16; scale; causal and window as in fa_fwd.
@@ -253,8 +253,8 @@ typedef struct {
 } fa_kvcache_params;
 
 /* Bytes of workspace fa_fwd_kvcache needs: float32 partial outputs and LSEs
- * of every part, B * nheads_q * Nq * parts * (headdim + 1) floats, rounded
- * up to 256 bytes. */
+ * of every part, B * nheads_q * Nq * parts * (Dk + 1) floats, rounded up to
+ * 256 bytes, where Dk = 64 for headdim <= 64 and 128 otherwise. */
 fa_status fa_fwd_kvcache_workspace_size(const fa_kvcache_params* params, size_t* bytes);
 
 /*
@@ -272,8 +272,8 @@ fa_status fa_fwd_kvcache_workspace_size(const fa_kvcache_params* params, size_t*
  *   k_new, v_new [in] both NULL (no append) or both given
  *   o [out] like q; lse [out] float32 (batch, nheads_q, Nq)
  *   workspace [scratch] fa_fwd_kvcache_workspace_size bytes, caller-owned
- * Rows with no visible key get o = 0 and lse = -inf.  fp32 and head sizes
- * other than 64/128 return FA_ERR_UNSUPPORTED.  Asynchronous on stream.
+ * Rows with no visible key get o = 0 and lse = -inf.  fp32 returns
+ * FA_ERR_UNSUPPORTED.  Asynchronous on stream.
  */
 fa_status fa_fwd_kvcache(const fa_kvcache_params* params, const void* q, void* k_cache, void* v_cache,
                          const int32_t* cache_seqlens, const void* k_new, const void* v_new, void* o,

@@ -141,9 +141,13 @@ INVALID = [
     ("reserved_mod set", dict(reserved_mod=1)),
 ]
 UNSUPPORTED = [
-    ("bf16 headdim 96", dict(headdim=96, q_strides=(64 * 4 * 96, 4 * 96, 96), o_strides=(64 * 4 * 96, 4 * 96, 96),
-                            k_strides=(64 * 2 * 96, 2 * 96, 96), v_strides=(64 * 2 * 96, 2 * 96, 96))),
-    ("fp16 headdim 32", dict(dtype=1, headdim=32)),
+    ("bf16 headdim 136", dict(headdim=136, q_strides=(64 * 4 * 136, 4 * 136, 136),
+                              o_strides=(64 * 4 * 136, 4 * 136, 136), k_strides=(64 * 2 * 136, 2 * 136, 136),
+                              v_strides=(64 * 2 * 136, 2 * 136, 136))),
+    ("fp16 headdim 256", dict(dtype=1, headdim=256, q_strides=(64 * 4 * 256, 4 * 256, 256),
+                              o_strides=(64 * 4 * 256, 4 * 256, 256), k_strides=(64 * 2 * 256, 2 * 256, 256),
+                              v_strides=(64 * 2 * 256, 2 * 256, 256))),
+    ("bf16 headdim 60", dict(headdim=60)),
     ("fp32 headdim 6", dict(dtype=0, headdim=6)),
     ("fp32 headdim 132", dict(dtype=0, headdim=132)),
     ("stride not 16 bytes", dict(k_strides=(64 * 2 * 64, 2 * 64, 68))),
@@ -331,9 +335,9 @@ def test_kvcache_specific_validation(lib):
 
 @pytest.mark.parametrize("name,kw", [
     ("fp32", dict(dtype=0)),
-    ("headdim 96", dict(headdim=96, q_strides=(4 * 96, 4 * 96, 96), o_strides=(4 * 96, 4 * 96, 96),
-                        k_strides=(256 * 2 * 96, 2 * 96, 96), v_strides=(256 * 2 * 96, 2 * 96, 96),
-                        knew_strides=(2 * 96, 2 * 96, 96), vnew_strides=(2 * 96, 2 * 96, 96))),
+    ("headdim 144", dict(headdim=144, q_strides=(4 * 144, 4 * 144, 144), o_strides=(4 * 144, 4 * 144, 144),
+                         k_strides=(256 * 2 * 144, 2 * 144, 144), v_strides=(256 * 2 * 144, 2 * 144, 144),
+                         knew_strides=(2 * 144, 2 * 144, 144), vnew_strides=(2 * 144, 2 * 144, 144))),
     ("new-row stride not 16 bytes", dict(knew_strides=(2 * 64, 2 * 64, 60))),
     ("negative new-row stride", dict(vnew_strides=(-128, 128, 64))),
 ])
@@ -503,3 +507,13 @@ def test_paged_kvcache_validation(lib):
 def test_paged_kvcache_valid_call_without_gpu_reports_hip_error(lib):
     assert call_paged(lib, kv_params()) == N.FA_ERR_HIP
     assert call_paged(lib, kv_params(), page_size=256, bt_stride=1) == N.FA_ERR_HIP
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-GPU error path")
+@pytest.mark.parametrize("d", [8, 32, 40, 96, 120])
+def test_head_dims_multiple_of_8_pass_validation(lib, d):
+    kw = dict(headdim=d, q_strides=(64 * 4 * d, 4 * d, d), o_strides=(64 * 4 * d, 4 * d, d),
+              k_strides=(64 * 2 * d, 2 * d, d), v_strides=(64 * 2 * d, 2 * d, d))
+    for dt in (N.FA_F16, N.FA_BF16):
+        assert call_fwd(lib, params(dtype=dt, **kw)) == N.FA_ERR_HIP
+        assert call_bwd(lib, params(dtype=dt, **kw)) == N.FA_ERR_HIP

@@ -238,10 +238,11 @@ def test_kvcache_rejects_fp32_and_odd_head_sizes():
     with pytest.raises(fa.FaError, match="UNSUPPORTED"):
         fa.fwd_kvcache(torch.zeros(1, 1, 1, 64, device="cuda"), c, c, torch.zeros(1, dtype=torch.int32,
                                                                                     device="cuda"))
-    c = torch.zeros(1, 64, 1, 96, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(fa.FaError, match="UNSUPPORTED"):
-        fa.fwd_kvcache(torch.zeros(1, 1, 1, 96, dtype=torch.bfloat16, device="cuda"), c, c,
-                       torch.zeros(1, dtype=torch.int32, device="cuda"))
+    for d in (136, 256, 100):  # above 128, or not a multiple of 8
+        c = torch.zeros(1, 64, 1, d, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(fa.FaError, match="UNSUPPORTED"):
+            fa.fwd_kvcache(torch.zeros(1, 1, 1, d, dtype=torch.bfloat16, device="cuda"), c, c,
+                           torch.zeros(1, dtype=torch.int32, device="cuda"))
 
 
 # ---------------------------------------------------------------------------
