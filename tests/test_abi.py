@@ -517,3 +517,20 @@ def test_head_dims_multiple_of_8_pass_validation(lib, d):
     for dt in (N.FA_F16, N.FA_BF16):
         assert call_fwd(lib, params(dtype=dt, **kw)) == N.FA_ERR_HIP
         assert call_bwd(lib, params(dtype=dt, **kw)) == N.FA_ERR_HIP
+
+
+def test_plain_c_caller_builds_and_links(tmp_path, lib):
+    # tests/c_caller/fa_c_caller.c uses only include/fa.h and the HIP runtime;
+    # it must compile as C99 and link against the library (run on a GPU in
+    # tests/test_c_caller_gpu.py).
+    import shutil
+    if shutil.which("gcc") is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or the ROCm headers are not available")
+    exe = tmp_path / "fa_c_caller"
+    libdir = os.path.dirname(N.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "c_caller", "fa_c_caller.c"),
+                    "-o", str(exe), "-L", libdir, "-lfa", "-L", "/opt/rocm/lib", "-lamdhip64", "-lm",
+                    f"-Wl,-rpath,{libdir}", "-Wl,-rpath,/opt/rocm/lib"], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 1 and "usage" in out.stderr
