@@ -89,8 +89,8 @@ def flops(w):
 # built from the sources whose SHA-256 is recorded here and are reported as
 # null for any other source.
 DKDV_TRAFFIC = {
-    "sources_sha256": "7dd81866cd5d55f3de3c5da8ec733d9fd88ae83fe6fc8a210d1a7fd83ecb8525",
-    "bytes_per_launch": 2252646893,
+    "sources_sha256": "154cf44552e24bcd0f8a24c5fe4aadc723a6f3d7540da4c914ecf4b54f38c1b3",
+    "bytes_per_launch": 2411319315,
 }
 
 
