@@ -217,11 +217,10 @@ struct DkdvWs {
 
   // S = Q K^T and dP = dO V^T of one item, 16 d-columns (one step st) at a
   // time; the row chunks of step st + NB - 1 are read while the MFMAs of step
-  // st run.  mid() runs once the MFMAs of the first two steps are issued.
-  template <class Mid>
+  // st run.
   __device__ __forceinline__ void score_products(const char* Qs, const char* dOs, const u32x4 (&kf)[D / 16],
                                                  const u32x4 (&vf)[D / 16], f32x16 (&s)[BMQ / 32],
-                                                 f32x16 (&dp)[BMQ / 32], Mid&& mid) {
+                                                 f32x16 (&dp)[BMQ / 32]) {
     constexpr int NST = D / 16, NB = 3;
     u32x4 qo[NB][BMQ / 32], go[NB][BMQ / 32];
 #pragma unroll
@@ -250,7 +249,6 @@ struct DkdvWs {
         dp[qb] = T::mfma(go[st % NB][qb], vf[st], dp[qb]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (st == 1) mid();
     }
   }
 
@@ -289,14 +287,11 @@ struct DkdvWs {
                                              const u32x4 (&kf)[D / 16], const u32x4 (&vf)[D / 16]) {
     // [qb][r] is query i0 + 32*qb + 8*(r/4) + 4*hf + r%4.
     f32x16 s[BMQ / 32], dp[BMQ / 32];
-    auto load_next = [&]() {
-      if (w + 1 < n_items) issue(nx, nslot);
-    };
-    if (w < n_items) {
-      score_products(slot_tiles(slot), slot_tiles(slot) + L::TILE * 2, kf, vf, s, dp, load_next);
-    } else {
-      load_next();
-    }
+    // The next item's loads go out before this item's products: a wave's
+    // loads issue slowly while another wave of its SIMD streams MFMAs, and
+    // here the gradient waves are not yet running theirs.
+    if (w + 1 < n_items) issue(nx, nslot);
+    if (w < n_items) score_products(slot_tiles(slot), slot_tiles(slot) + L::TILE * 2, kf, vf, s, dp);
     lds_barrier();  // the gradient waves have taken the previous item's P and dS
     if (w < n_items) {
       const int i0 = row_of(cu);

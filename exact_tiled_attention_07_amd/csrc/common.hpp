@@ -229,8 +229,19 @@ struct F16 {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value of the lane 32 positions away (lanes l and l^32 of a wave64).
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Reductions over the lane pair (l, l^32) of a wave64.  One
+// v_permlane32_swap of x with itself leaves {x[l], x[l^32]} in its two
+// results (in an order that depends on the half), so max and sum need no LDS
+// round trip; the sum has the same two operands in both lanes of the pair and
+// is therefore the same bits in both.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // ---------------------------------------------------------------------------
 // Workgroup -> work-item decode.  On MI355X consecutive workgroup ids are

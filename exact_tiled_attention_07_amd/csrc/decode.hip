@@ -258,10 +258,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
       const int key = j0 + 8 * (r >> 2) + 4 * hf + (r & 3);
       if (key < lo_r || key > hi_r) sv[r] = -INFINITY;
     }
-    float mx = -INFINITY;
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[r]);
-    mx = fmaxf(mx, xor32(mx));
+    for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], sv[r]);
+    const float mx = max_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
     if (__any((mx - mref) * cs > kKvLazyRescale)) {
       const float m_new = fmaxf(mref, mx);
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((mref - m_new) * cs);
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
   }
 
   // Partial result of this part: O / l and LSE (natural log), per row.
-  const float lt = l + xor32(l);
+  const float lt = sum_xor32(l);
   if (valid) {
     const int64_t row = ((int64_t)(b * k.Hq + hq) * k.Nq + i) * k.S + s;
     if (hf == 0) k.ws_lse[row] = (lt > 0.f) ? (mref * k.scale + logf(lt)) : -INFINITY;

@@ -57,11 +57,13 @@ static constexpr float kLazyRescale = 8.0f;
 //     interval 2m+1:  A  softmax(m)     B  MFMA(m)
 // so on every SIMD one wave feeds the matrix core while the other does the
 // softmax.  K(m) is read in intervals 2m and 2m+1, V(m) in 2m+2 and 2m+3,
-// each from two LDS buffers.  Group A loads K(m+1) and V(m) at the end of
-// its MFMA interval 2m (after its last transposing read of the interval,
-// which the compiler would otherwise hold for the loads), into the buffers
-// whose last readers finished in interval 2m-1, and waits for them at the
-// end of interval 2m+1.
+// each from two LDS buffers.  The tile loads are split between the groups so
+// that neither MFMA interval carries all of their issue cost: group A loads
+// K(m+1) at the end of its MFMA interval 2m, group B loads V(m+1) at the end
+// of its MFMA interval 2m+1 (both after the interval's last transposing read,
+// which the compiler would otherwise hold for the loads), each into a buffer
+// whose last reader has finished, and each group waits for its loads at the
+// end of its next (softmax) interval.
 // ---------------------------------------------------------------------------
 template <class T, int D, int BN, bool MOD>
 struct FwdPP {
@@ -132,11 +134,15 @@ struct FwdPP {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Group A's tile loads, after the last transposing read of the interval
-    // (issued in one burst: spread between the S products they stall them).
+    // Tile loads, after the last transposing read of the interval (issued in
+    // one burst: spread between the S products they stall them).  Group A
+    // loads K(m+1) into the K buffer read in intervals 2m-2 and 2m-1; group B
+    // loads V(m+1) into the V buffer whose last reader is this very interval
+    // (B's product with V(m-1); A's was in interval 2m).
     if (group_a) {
       if (m + 1 < n) kd.issue(Kp, k_sn, (t_lo + m + 1) * BN, Nk, kbuf + (1 - PAR) * TILE, wave);
-      if (m < n) vd.issue(Vp, v_sn, (t_lo + m) * BN, Nk, vbuf + PAR * TILE, wave);
+    } else {
+      if (m + 1 < n) vd.issue(Vp, v_sn, (t_lo + m + 1) * BN, Nk, vbuf + (1 - PAR) * TILE, wave - HALF);
     }
   }
 
@@ -168,13 +174,14 @@ struct FwdPP {
     // The reference maximum moves only when some row of the wave grew by more
     // than 2^kLazyRescale; then O and l (which hold the tiles up to m - 1) are
     // rescaled.
-    float mx = -INFINITY;
+    // Row maximum: four independent chains, then the lane pair.
+    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
     }
-    mx = fmaxf(mx, xor32(mx));
+    const float mx = max_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
     if (__any((mx - mref) * c > kLazyRescale)) {  // false for NaN (both -inf)
       const float m_new = fmaxf(mref, mx);
       const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((mref - m_new) * c);
@@ -184,6 +191,8 @@ struct FwdPP {
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
     }
     const float mc = (mref == -INFINITY) ? 0.f : mref * c;
+    // Row sum of this tile in four partial sums (short dependency chains).
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
@@ -192,11 +201,12 @@ struct FwdPP {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           p[e] = fast_exp2(fmaf(s[kb][8 * tt + e], c, -mc));
-          l += p[e];
+          l4[e & 3] += p[e];
         }
         pf[2 * kb + tt] = u32x4{T::pack(p[0], p[1]), T::pack(p[2], p[3]), T::pack(p[4], p[5]), T::pack(p[6], p[7])};
       }
     }
+    l += (l4[0] + l4[1]) + (l4[2] + l4[3]);
   }
 };
 
@@ -289,10 +299,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int i = 0; i < TILE * 2 / (512 * 16); ++i)
     reinterpret_cast<u32x4*>(vbuf + TILE)[i * 512 + tid] = u32x4{0u, 0u, 0u, 0u};
 
-  x.kd.init(wave, lane, a.k_sn, a.D / 8);
-  x.vd.init(wave, lane, a.v_sn, a.D / 8);
-  if (group_a && x.n > 0) {
-    x.kd.issue(x.Kp, a.k_sn, x.t_lo * BN, a.Nk, kbuf, wave);
+  // Group A loads the K tiles, group B the V tiles; K(0) and V(0) here.
+  x.kd.init(wave % Ctx::HALF, lane, a.k_sn, a.D / 8);
+  x.vd.init(wave % Ctx::HALF, lane, a.v_sn, a.D / 8);
+  if (x.n > 0) {
+    if (group_a)
+      x.kd.issue(x.Kp, a.k_sn, x.t_lo * BN, a.Nk, kbuf, wave);
+    else
+      x.vd.issue(x.Vp, a.v_sn, x.t_lo * BN, a.Nk, vbuf, wave - Ctx::HALF);
     wait_all_loads();
   }
   __syncthreads();
@@ -323,16 +337,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   } else {
     for (; m + 1 <= n; m += 2) {
       x.softmax_interval(m - 1);
+      wait_all_loads();
       lds_barrier();
       x.template mfma_interval<0>(m, false);
       lds_barrier();
       x.softmax_interval(m);
+      wait_all_loads();
       lds_barrier();
       x.template mfma_interval<1>(m + 1, false);
       lds_barrier();
     }
     if (m <= n) {
       x.softmax_interval(m - 1);
+      wait_all_loads();
       lds_barrier();
       x.template mfma_interval<0>(m, false);
       lds_barrier();
@@ -341,7 +358,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // Epilogue: O = O / l, LSE = scale*mref + ln(l).  Lanes l and l^32 hold
   // different keys of the same query, so their partial sums are added here.
-  const float lt = x.l + xor32(x.l);
+  const float lt = sum_xor32(x.l);
   const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
   if (qrow < a.Nq) {
     uint16_t* op = static_cast<uint16_t*>(a.o) + b * a.o_sb + hq * a.o_sh + (int64_t)qrow * a.o_sn;
