@@ -137,8 +137,9 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
 //                  Q^T read transposed from the item's tiles.
 // Score wave k and gradient wave KW + k share a SIMD.  Each item takes two
 // barriers: before the first the score waves run their MFMAs while the
-// gradient waves fetch P and dS; after it the gradient waves run their MFMAs
-// while the score waves do the exponentials.  So the matrix core of every SIMD
+// gradient waves fetch P and dS (both groups first issue their share of the
+// next item's tile loads); after it the gradient waves run their MFMAs while
+// the score waves do the exponentials.  So the matrix core of every SIMD
 // always has one wave feeding it, and the vector work hides behind it.
 // Q/dO tiles rotate through three LDS slots (the item being scored, the item
 // being accumulated, and the next item's loads in flight); P/dS need one
@@ -167,11 +168,13 @@ struct DkdvWs {
   int b, hk, k0, k_last, key, qt_lo, n_qt, n_items, wave, kb, lane, hf;
   float c;
   SwzOffsets<D> off;
-  // The score waves issue every tile load.  (A wave whose transposing LDS
-  // reads follow its own direct-to-LDS loads in program order is made to wait
-  // for those loads by the compiler, even where they cannot overlap; the
-  // score waves read LDS only with plain reads, which the compiler orders by
-  // the explicit waits and barriers here.)
+  // The score waves load the Q tiles and row statistics, the gradient waves
+  // the dO tiles, both at the start of an item (a wave's loads issue slowly
+  // while another wave of its SIMD streams MFMAs, and neither group runs
+  // MFMAs there yet).  A wave whose transposing LDS reads follow its own
+  // direct-to-LDS loads in program order is made to wait for those loads by
+  // the compiler, even where they cannot overlap; the gradient waves wait for
+  // theirs before the item's first barrier anyway.
   DmaTile<D, BMQ, L::KW> qd, dd;
 
   // Work items run over query tiles from the last one down, with the heads of
@@ -192,15 +195,19 @@ struct DkdvWs {
   __device__ __forceinline__ char* slot_tiles(int slot) const { return smem + slot * L::SLOT; }
   __device__ __forceinline__ char* slot_stats(int slot) const { return smem + L::OFF_RST + slot * L::RST; }
 
-  // Score wave kb loads its share of one item's Q and dO tiles (and wave
-  // KW-1 the item's row statistics) into slot `slot`.
+  // Wave kb of a group loads its share of one item's Q tile (and wave KW-1
+  // the item's row statistics) if Q, and of its dO tile if DO, into slot
+  // `slot`.
+  template <bool Q, bool DO>
   __device__ __forceinline__ void issue(const Cursor& cu, int slot) {
     const int i0 = row_of(cu), hq = hk * a->G + cu.g;
-    qd.issue(static_cast<const uint16_t*>(a->q) + b * a->q_sb + hq * a->q_sh, a->q_sn, i0, a->Nq,
-             reinterpret_cast<uint16_t*>(slot_tiles(slot)), kb);
-    dd.issue(static_cast<const uint16_t*>(a->dout) + b * a->o_sb + hq * a->o_sh, a->o_sn, i0, a->Nq,
-             reinterpret_cast<uint16_t*>(slot_tiles(slot) + L::TILE * 2), kb);
-    if (kb == L::KW - 1) {
+    if (Q)
+      qd.issue(static_cast<const uint16_t*>(a->q) + b * a->q_sb + hq * a->q_sh, a->q_sn, i0, a->Nq,
+               reinterpret_cast<uint16_t*>(slot_tiles(slot)), kb);
+    if (DO)
+      dd.issue(static_cast<const uint16_t*>(a->dout) + b * a->o_sb + hq * a->o_sh, a->o_sn, i0, a->Nq,
+               reinterpret_cast<uint16_t*>(slot_tiles(slot) + L::TILE * 2), kb);
+    if (Q && kb == L::KW - 1) {
       const int64_t ro = b * a->ws_sb + hq * a->ws_sh + i0;
       uint16_t* r = reinterpret_cast<uint16_t*>(slot_stats(slot));
       if (lane < BMQ / 4) {
@@ -287,10 +294,8 @@ struct DkdvWs {
                                              const u32x4 (&kf)[D / 16], const u32x4 (&vf)[D / 16]) {
     // [qb][r] is query i0 + 32*qb + 8*(r/4) + 4*hf + r%4.
     f32x16 s[BMQ / 32], dp[BMQ / 32];
-    // The next item's loads go out before this item's products: a wave's
-    // loads issue slowly while another wave of its SIMD streams MFMAs, and
-    // here the gradient waves are not yet running theirs.
-    if (w + 1 < n_items) issue(nx, nslot);
+    // The next item's Q tile goes out before this item's products.
+    if (w + 1 < n_items) issue<true, false>(nx, nslot);
     if (w < n_items) score_products(slot_tiles(slot), slot_tiles(slot) + L::TILE * 2, kf, vf, s, dp);
     lds_barrier();  // the gradient waves have taken the previous item's P and dS
     if (w < n_items) {
@@ -319,7 +324,7 @@ struct DkdvWs {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int i = i0 + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key < key_lo(*a, i) || key > key_hi(*a, i)) s[qb][r] = -INFINITY;
+            if ((key < key_lo(*a, i)) | (key > key_hi(*a, i))) s[qb][r] = -INFINITY;
           }
         }
       }
@@ -360,9 +365,14 @@ struct DkdvWs {
     nx.next(a->G);
   }
 
-  // One item of a gradient wave: accumulate item w - 1 (slot `pslot`).
-  __device__ __forceinline__ void grad_step(int w, int pslot, f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
+  // One item of a gradient wave: load the dO tile of item w + 1 (cursor nx)
+  // into slot nslot, which held item w - 2; accumulate item w - 1 (slot
+  // `pslot`).
+  __device__ __forceinline__ void grad_step(int w, int pslot, int nslot, Cursor& nx, f32x16 (&dka)[D / 32],
+                                            f32x16 (&dva)[D / 32]) {
     u32x4 pf[BMQ / 16], dsf[BMQ / 16];
+    if (w + 1 < n_items) issue<false, true>(nx, nslot);
+    nx.next(a->G);
     if (w >= 1) {
       const char* pimg = img(0);
       const char* dimg = img(1);
@@ -372,7 +382,8 @@ struct DkdvWs {
         dsf[si] = *reinterpret_cast<const u32x4*>(dimg + si * 1024);
       }
     }
-    lds_barrier();  // P/dS of item w - 1 are in registers
+    wait_all_loads();  // this wave's share of item w + 1 has landed (before any transposing read)
+    lds_barrier();     // P/dS of item w - 1 are in registers
     if (w >= 1) grad_products(slot_tiles(pslot), slot_tiles(pslot) + L::TILE * 2, pf, dsf, dka, dva);
     lds_barrier();
   }
@@ -406,9 +417,11 @@ struct DkdvWs {
   __device__ __forceinline__ void grad_loop(f32x16 (&dka)[D / 32], f32x16 (&dva)[D / 32]) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dka[db] = dva[db] = f32x16{};
+    Cursor nx{0, 0};
+    nx.next(a->G);             // cursor of item w + 1
     int pslot = L::NSLOT - 1;  // slot of item w - 1
     for (int w = 0; w <= n_items; ++w) {
-      grad_step(w, pslot, dka, dva);
+      grad_step(w, pslot, pslot == 0 ? 2 : pslot - 1, nx, dka, dva);  // item w + 1 sits where w - 2 did
       pslot = (pslot == L::NSLOT - 1) ? 0 : pslot + 1;
     }
   }
@@ -452,7 +465,7 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
   x.dd.init(x.kb, lane, a.o_sn, a.D / 8);
 
   if (x.n_items > 0 && wave < L::KW) {
-    x.issue(typename DkdvWs<T, D, BMQ, MOD>::Cursor{0, 0}, 0);
+    x.template issue<true, true>(typename DkdvWs<T, D, BMQ, MOD>::Cursor{0, 0}, 0);
     wait_all_loads();
   }
   __syncthreads();
