@@ -210,10 +210,9 @@ struct DkdvWs {
     if (Q && kb == L::KW - 1) {
       const int64_t ro = b * a->ws_sb + hq * a->ws_sh + i0;
       uint16_t* r = reinterpret_cast<uint16_t*>(slot_stats(slot));
-      if (lane < BMQ / 4) {
-        dma16(a->lse2 + ro + 4 * lane, r);
-      } else if (lane < BMQ / 2) {
-        dma16(a->dsum + ro + 4 * (lane - BMQ / 4), r);
+      if (lane < BMQ / 4) {  // lse2[BMQ] then dsum[BMQ]
+        buffer_dma16(raw_rsrc(a->lse2 + ro, BMQ * 4), 16 * lane, r);
+        buffer_dma16(raw_rsrc(a->dsum + ro, BMQ * 4), 16 * lane, r + BMQ * 2);
       }
     }
   }
@@ -324,7 +323,7 @@ struct DkdvWs {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int i = i0 + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if ((key < key_lo(*a, i)) | (key > key_hi(*a, i))) s[qb][r] = -INFINITY;
+            if (int(key < key_lo(*a, i)) | int(key > key_hi(*a, i))) s[qb][r] = -INFINITY;
           }
         }
       }

@@ -91,23 +91,43 @@ __device__ __forceinline__ u32x4 load_cols(const uint16_t* row, int col, int dh)
 }
 
 // ===========================================================================
-// Direct global -> LDS tile loads (global_load_lds_dwordx4).
+// Direct global -> LDS tile loads (buffer_load_dwordx4 ... lds).
 //
 // One instruction moves 16 bytes per lane into LDS at (wave-uniform base) +
 // 16 * lane, i.e. 1 KB of consecutive LDS per wave.  The swizzled layout above
-// is produced by choosing each lane's global address: LDS chunk slot `lane` of
+// is produced by choosing each lane's source offset: LDS chunk slot `lane` of
 // 1 KB block j is row j*RPB + lane / CPR, physical chunk lane % CPR, which
 // holds logical chunk (lane % CPR) ^ sw(row).  Each lane's byte offsets
 // (relative to the tile's first row) are computed once per kernel; a tile
-// load then adds one wave-uniform base pointer.
+// load then builds one buffer resource from scalars.
+//
+// The buffer form addresses memory with a scalar resource plus one 32-bit
+// lane offset.  On MI355X it issues in about the same time whether or not
+// another wave of the SIMD is streaming MFMAs, while global_load_lds with
+// 64-bit per-lane addresses measured up to 40x slower to issue in that case.
+// Rows past the end of the tensor lie outside the resource's range and read
+// as zeros (those keys or queries are masked, and 0 * 0 stays finite).
 // ===========================================================================
-// 16 bytes per lane from global memory straight into LDS at
+// Word 3 of a raw buffer resource on this chip family (32-bit data format, no
+// swizzle, no stride): loads at or past num_records bytes return zeros.
+static constexpr int kRawBufferWord3 = 0x00020000;
+
+// The base and size must be the same in every lane; they are read from the
+// first lane, so the resource sits in scalar registers (the compiler cannot
+// always prove such values uniform and would otherwise loop over lanes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), kRawBufferWord3);
+}
+
+// 16 bytes per lane at byte offset voff of resource rs straight into LDS at
 // lds_block + 16 * lane (lds_block must be the same for the whole wave).
-// (Forcing the scalar-base form, a wave-uniform global base in SGPRs plus a
-// 32-bit lane offset and the LDS base taken from the first lane, measured
-// slower on MI355X for every kernel here.)
-__device__ __forceinline__ void dma16(const void* g, const void* lds_block) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_block, 16, 0, 0);
+__device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, const void* lds_block) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_block, 16, (int)voff, 0,
+                                           0, 0);
 }
 
 template <int D, int ROWS, int NW>
@@ -118,16 +138,14 @@ struct DmaTile {
   static constexpr int PER_WAVE = (NBLK + NW - 1) / NW;
   static_assert(ROWS % RPB == 0, "tile rows must fill whole 1 KB blocks");
   uint32_t off[PER_WAVE];  // byte offsets of this lane's chunk in each of its blocks
-  int lane_row, lane_pc, dch;
 
   // dch = 16-byte chunks of a row that hold data (head dim / 8, <= D / 8).  A
   // lane whose chunk lies past it loads chunk 0 of the same row instead (valid
   // memory, no per-load test): the kernels pair those LDS columns only with
-  // zero register columns or with outputs that are never stored.
-  __device__ __forceinline__ void init(int wave, int lane, int64_t row_stride_elems, int dch_ = D / 8) {
-    lane_row = lane / CPR;
-    lane_pc = lane % CPR;
-    dch = dch_;
+  // zero register columns or with outputs that are never stored.  Row strides
+  // are at most 2^22 elements, so every offset fits 32 bits.
+  __device__ __forceinline__ void init(int wave, int lane, int64_t row_stride_elems, int dch = D / 8) {
+    const int lane_row = lane / CPR, lane_pc = lane % CPR;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int j = wave + i * NW;
@@ -137,29 +155,16 @@ struct DmaTile {
     }
   }
   // Rows row0 .. row0+ROWS-1 of a tensor whose rows start every row_stride
-  // elements.  Rows at or beyond nrows (>= 1) re-read row nrows-1 (those keys
-  // are masked; a finite copy keeps 0 * value finite).
+  // elements; rows at or beyond nrows read as zeros.
   __device__ __forceinline__ void issue(const uint16_t* base, int64_t row_stride, int row0, int nrows,
                                         uint16_t* lds_tile, int wave) const {
-    const char* tb = reinterpret_cast<const char*>(base + (int64_t)row0 * row_stride);
-    if (row0 + ROWS <= nrows) {
+    const int rows = min(max(nrows - row0, 0), ROWS);
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(base + (int64_t)row0 * row_stride, (uint32_t)(rows * row_stride * 2));
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i) {
-        const int j = wave + i * NW;
-        if (NBLK % NW == 0 || j < NBLK) dma16(tb + off[i], lds_tile + j * 512);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i) {
-        const int j = wave + i * NW;
-        if (NBLK % NW == 0 || j < NBLK) {
-          const int r = j * RPB + lane_row;
-          const int row = min(row0 + r, nrows - 1);
-          int c = lane_pc ^ Swz<D>::sw(r);
-          c = c < dch ? c : 0;
-          dma16(reinterpret_cast<const char*>(base + (int64_t)row * row_stride) + c * 16, lds_tile + j * 512);
-        }
-      }
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int j = wv + i * NW;
+      if (NBLK % NW == 0 || j < NBLK) buffer_dma16(rs, off[i], lds_tile + j * 512);
     }
   }
 };
