@@ -89,8 +89,8 @@ def flops(w):
 # built from the sources whose SHA-256 is recorded here and are reported as
 # null for any other source.
 DKDV_TRAFFIC = {
-    "sources_sha256": "154cf44552e24bcd0f8a24c5fe4aadc723a6f3d7540da4c914ecf4b54f38c1b3",
-    "bytes_per_launch": 2411319315,
+    "sources_sha256": "0e427f67624b2a1ff398ed23fcf7b94bd8e88c39910a0bb03d355d8bf21558ba",
+    "bytes_per_launch": 2068674897,
 }
 
 
