@@ -202,6 +202,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
   auto ld = [](const uint16_t* p) -> u32x4 {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   };
+  // Tiles that lie wholly in the cache (all but at most the last two of a
+  // range) load through buffer resources: one scalar base per tile plus fixed
+  // 32-bit lane offsets, which issue without the 64-bit address arithmetic
+  // per chunk (and without stalling behind other waves' MFMAs).
+  // Chunk c of a lane is row crow[0] + c * (512 / D) of the tile: the lane part
+  // of the offset is fixed, the chunk part is a scalar.
+  static_assert(64 % (D / 8) == 0, "chunk rows step by a whole number of rows");
+  const uint32_t koff = (uint32_t)(crow[0] * k.kc_sn * 2 + 16 * cload);
+  const uint32_t voff = (uint32_t)(crow[0] * k.vc_sn * 2 + 16 * cload);
+  auto ld_tile = [&](const uint16_t* kb, const uint16_t* vb, KvStage<D>& st) {
+    const __amdgpu_buffer_rsrc_t rk = raw_rsrc(kb, (uint32_t)(32 * k.kc_sn * 2));
+    const __amdgpu_buffer_rsrc_t rv = raw_rsrc(vb, (uint32_t)(32 * k.vc_sn * 2));
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ks = c * (512 / D) * (int)k.kc_sn * 2, vs = c * (512 / D) * (int)k.vc_sn * 2;
+      st.kr[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)koff, ks, kNonTemporal));
+      st.vr[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)voff, vs, kNonTemporal));
+    }
+  };
   // Rows past the end of the keys repeat the last one (their scores are masked).
   auto load_tile = [&](int t, KvStage<D>& st) {
     if constexpr (PAGED) {
@@ -211,6 +230,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
       const int r0 = p * k.page_size;
       const uint16_t* Kp = Kc + pg * k.kc_sb;
       const uint16_t* Vp = Vc + pg * k.vc_sb;
+      if (32 * t + 31 < L) {
+        ld_tile(Kp + (int64_t)(32 * t - r0) * k.kc_sn, Vp + (int64_t)(32 * t - r0) * k.vc_sn, st);
+        return;
+      }
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const int j = min(32 * t + crow[c], Lk - 1);
@@ -218,6 +241,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FA_KV_WAVES)
         st.vr[c] = ld((j < L ? Vp + (int64_t)(j - r0) * k.vc_sn : Vn + (int64_t)(j - L) * k.vn_sn) + 8 * cload);
       }
     } else {
+      if (32 * t + 31 < L) {
+        ld_tile(Kc + (int64_t)(32 * t) * k.kc_sn, Vc + (int64_t)(32 * t) * k.vc_sn, st);
+        return;
+      }
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const int j = min(32 * t + crow[c], Lk - 1);

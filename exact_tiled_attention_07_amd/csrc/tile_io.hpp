@@ -111,6 +111,8 @@ __device__ __forceinline__ u32x4 load_cols(const uint16_t* row, int col, int dh)
 // Word 3 of a raw buffer resource on this chip family (32-bit data format, no
 // swizzle, no stride): loads at or past num_records bytes return zeros.
 static constexpr int kRawBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer load: the non-temporal hint.
+static constexpr int kNonTemporal = 2;
 
 // The base and size must be the same in every lane; they are read from the
 // first lane, so the resource sits in scalar registers (the compiler cannot
