@@ -175,6 +175,24 @@ def test_bitwise_repeatable(dtype):
         assert torch.equal(a, b)
 
 
+def test_bitwise_repeatable_bench_workload():
+    # The benchmark workload at full size, four forward + backward passes: every
+    # output equal to the first pass's bit for bit (no atomics, no data races on
+    # the LDS buffers the tile loads rotate through).
+    w = WORKLOADS["bf16_b2_hq32_hkv8_n8192_d128_causal"]
+    q, k, v, do = (t.cuda() for t in make_inputs(w))
+    ref = None
+    for _ in range(4):
+        o, lse = fa.fwd(q, k, v, causal=True)
+        outs = (o, lse) + tuple(fa.bwd(do, q, k, v, o, lse, causal=True))
+        torch.cuda.synchronize()
+        if ref is None:
+            ref = [t.clone() for t in outs]
+            continue
+        for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), ref, outs):
+            assert torch.equal(a, b), name
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 def test_backward_stages_equal_fa_bwd(dtype):
     # fa_bwd_stage PREPARE then DQ then DKDV (the two gradient stages in the
