@@ -89,8 +89,8 @@ def flops(w):
 # built from the sources whose SHA-256 is recorded here and are reported as
 # null for any other source.
 DKDV_TRAFFIC = {
-    "sources_sha256": "0e427f67624b2a1ff398ed23fcf7b94bd8e88c39910a0bb03d355d8bf21558ba",
-    "bytes_per_launch": 2068674897,
+    "sources_sha256": "ad5f6bdcd0b17e15bdbd914cd55dbf5f0929e8f6ebdc6c2e24e9fd34b0b9ea74",
+    "bytes_per_launch": 2098642319,
 }
 
 
