@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample (whole heads are added until it is reached)")
     ap.add_argument("--decode-calls", type=int, default=200, help="timed fa_fwd_kvcache calls (0: skip)")
+    ap.add_argument("--next-rows-steps", type=int, default=10,
+                    help="timed steps of the packed-batch and score-modifier legs (0: skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="instead of the benchmark, run a plain device copy of 512 MiB (read 512 MiB, "
                          "write 512 MiB) 5 times: the known-size reference for HBM byte counters")
@@ -89,8 +91,8 @@ def flops(w):
 # built from the sources whose SHA-256 is recorded here and are reported as
 # null for any other source.
 DKDV_TRAFFIC = {
-    "sources_sha256": "ad5f6bdcd0b17e15bdbd914cd55dbf5f0929e8f6ebdc6c2e24e9fd34b0b9ea74",
-    "bytes_per_launch": 2098642319,
+    "sources_sha256": "1b52644570859e75151f9a133a3496ac6187b6f63614937fa373d9f3900aa79f",
+    "bytes_per_launch": 2044942708,
 }
 
 
@@ -276,6 +278,87 @@ def decode_leg(calls):
     }
 
 
+# Sequence lengths of the packed-batch leg: 16384 tokens, as many as the
+# benchmark workload's two sequences of 8192, in a ragged mix.
+VARLEN_LENGTHS = [4096, 2560, 2048, 1792, 1536, 1280, 1024, 768, 512, 384, 256, 128]
+
+
+def next_rows_leg(steps):
+    """fwd + bwd throughput of two rows beyond the benchmark step, same heads
+    and head size (Hq=32, Hkv=8, d=128, bf16, causal), events on the launch
+    stream: a packed batch of VARLEN_LENGTHS through fa_fwd_varlen /
+    fa_bwd_varlen, and the benchmark workload with ALiBi slopes and a softcap
+    (the modifier kernels).  FLOP per causal sequence of length L: 4*Hq*d*L^2/2
+    forward, 2.5 times that backward."""
+    import torch
+
+    import exact_tiled_attention_07_amd as fa
+    from exact_tiled_attention_07_amd.workloads import BENCH_WORKLOAD, WORKLOADS, make_inputs
+
+    w = WORKLOADS[BENCH_WORKLOAD]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fwd_call, bwd_call):
+        for _ in range(3):
+            fwd_call()
+            bwd_call()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for e in ev:
+            e[0].record(stream)
+            fwd_call()
+            e[1].record(stream)
+            bwd_call()
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        return (sum(e[0].elapsed_time(e[1]) for e in ev) / steps, sum(e[1].elapsed_time(e[2]) for e in ev) / steps)
+
+    def entry(f_fwd, fwd_ms, bwd_ms):
+        tf = 3.5 * f_fwd / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
+        return {"fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+                "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2), "tflops": round(tf, 2),
+                "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+    out = {"steps": steps}
+    # Packed batch.
+    g = torch.Generator("cpu").manual_seed(w.seed + 17)
+    tot = sum(VARLEN_LENGTHS)
+    q, k, v, do = ((torch.randn((tot, h, w.headdim), generator=g) * sd).to(torch.bfloat16).to(dev)
+                   for h, sd in ((w.nheads_q, w.sigma), (w.nheads_kv, w.sigma), (w.nheads_kv, w.sigma),
+                                 (w.nheads_q, 1.0)))
+    cu = torch.tensor([0] + [int(x) for x in torch.tensor(VARLEN_LENGTHS).cumsum(0)], dtype=torch.int32, device=dev)
+    mx = max(VARLEN_LENGTHS)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.nheads_q, tot), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    vp = fa.make_varlen_params(q, k, v, o, mx, mx, causal=True, batch=len(VARLEN_LENGTHS))
+    vws = torch.empty(fa.bwd_varlen_workspace_size(vp), dtype=torch.uint8, device=dev)
+    fm, bm = timed(lambda: fa.fwd_varlen(q, k, v, cu, cu, mx, mx, causal=True, out=o, lse=lse),
+                   lambda: fa.bwd_varlen(do, q, k, v, o, lse, cu, cu, mx, mx, causal=True, dq=dq, dk=dk, dv=dv,
+                                         workspace=vws))
+    f_fwd = 4.0 * w.nheads_q * w.headdim * sum(L * L / 2 for L in VARLEN_LENGTHS)
+    out["varlen"] = {"entry_points": "fa_fwd_varlen + fa_bwd_varlen", "seqlens": VARLEN_LENGTHS,
+                     **entry(f_fwd, fm, bm)}
+    del q, k, v, do, o, lse, dq, dk, dv, vws
+    # Score modifiers on the benchmark workload.
+    q, k, v, do = (t.to(dev) for t in make_inputs(w))
+    slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / w.nheads_q) for h in range(w.nheads_q)], dtype=torch.float32,
+                          device=dev)
+    softcap = 30.0
+    kw = dict(causal=True, alibi_slopes=slopes, softcap=softcap)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.nheads_q, w.seqlen), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.bwd_workspace_size(fa.make_params(q, k, v, o, **kw)), dtype=torch.uint8, device=dev)
+    fm, bm = timed(lambda: fa.fwd(q, k, v, out=o, lse=lse, **kw),
+                   lambda: fa.bwd(do, q, k, v, o, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw))
+    f_fwd = flops(w)[0]
+    out["modifiers"] = {"workload": w.name, "alibi_slopes": "2^(-8(h+1)/Hq) per head", "softcap": softcap,
+                        **entry(f_fwd, fm, bm)}
+    return out
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -383,6 +466,8 @@ def main():
     }
     if args.decode_calls > 0:
         out["decode"] = decode_leg(args.decode_calls)
+    if args.next_rows_steps > 0:
+        out["next_rows"] = next_rows_leg(args.next_rows_steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q_c, k_c, v_c, do_c, args.cpu_seconds)
     print(json.dumps(out), flush=True)

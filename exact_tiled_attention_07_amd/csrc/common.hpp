@@ -77,7 +77,8 @@ struct AttnArgs {
 // then slope/scale * |i' - j| is subtracted; masking comes after.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float mod_score(float s, float cap, float slope_raw, float dist) {
-  return fmaf(-slope_raw, fabsf(dist), fminf(fmaxf(s, -cap), cap));
+  // One v_med3_f32 for the clamp (fminf/fmaxf would add NaN quieting).
+  return fmaf(-slope_raw, fabsf(dist), __builtin_amdgcn_fmed3f(s, -cap, cap));
 }
 // Slope of (b, h) in raw score units (0 without ALiBi).
 __device__ __forceinline__ float alibi_raw(const float* alibi, int64_t sb, float inv_scale, int b, int h) {
@@ -246,10 +247,13 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // ---------------------------------------------------------------------------
 // Workgroup -> work-item decode.  On MI355X consecutive workgroup ids are
 // dispatched round-robin over the 8 XCDs, each with its own L2.  With
-// xcd_remap, id w runs on XCD w % 8, and the work of that XCD is a contiguous
-// range of "units" (here (batch, kv head) pairs) so that the workgroups
-// sharing K/V also share an L2.  Inside an XCD the order is tile-major with
-// the heaviest tiles (largest causal prefix) first.
+// xcd_remap, id w runs on XCD w % 8, and every "unit" (a (batch, kv head)
+// pair) runs whole on one XCD, so that the workgroups sharing K/V also share
+// an L2.  XCD x takes the units x, x + 8, x + 16, ...: with the kv heads
+// innermost, every XCD then holds the same heads of every batch entry, which
+// balances the XCDs also when the sequences of a packed batch differ in
+// length.  Inside an XCD the order is tile-major with the heaviest tiles
+// (largest causal prefix) first.
 // ---------------------------------------------------------------------------
 struct WorkItem {
   int unit;   // (batch * Hkv + kv head)
@@ -269,7 +273,7 @@ __device__ __forceinline__ WorkItem decode_work(int w, int n_units, int n_tiles,
     const int t = slot / n_sub;
     ui = t % per;
     const int tr = t / per;
-    it.unit = xcd * per + ui;
+    it.unit = ui * 8 + xcd;
     it.tile = heavy_last_first ? (n_tiles - 1 - tr) : tr;
   } else {
     it.sub = w % n_sub;
