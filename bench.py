@@ -91,8 +91,8 @@ def flops(w):
 # built from the sources whose SHA-256 is recorded here and are reported as
 # null for any other source.
 DKDV_TRAFFIC = {
-    "sources_sha256": "1b52644570859e75151f9a133a3496ac6187b6f63614937fa373d9f3900aa79f",
-    "bytes_per_launch": 2044942708,
+    "sources_sha256": "f3dd78c97488e5da36e667ea15df8a60d564fff01042fc54de6bcc8db35f4b43",
+    "bytes_per_launch": 2081126083,
 }
 
 

@@ -109,6 +109,9 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
 #ifndef FA_DKDV_BMQ
 #define FA_DKDV_BMQ 64  // queries per dK/dV iteration
 #endif
+#ifndef FA_DKDV_GRING
+#define FA_DKDV_GRING 2  // transposed operand pairs in flight in the dK/dV gradient waves
+#endif
 #ifndef FA_DQ_RING
 #define FA_DQ_RING 3  // LDS operands in flight ahead of the MFMA that uses them
 #endif
@@ -131,10 +134,13 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
 //                  then P = exp2(s*c - lse2) and dS = P * (dP - D), and write P
 //                  and dS to LDS exactly as the B-operand registers they are
 //                  (16 bytes per lane);
-//   gradient waves (KW .. 2KW-1) hold the dK^T and dV^T accumulators of the
-//                  same keys; one item later they read P and dS back and
-//                  accumulate dV^T += dO^T P and dK^T += Q^T dS, with dO^T and
-//                  Q^T read transposed from the item's tiles.
+//   gradient waves (KW .. 2KW-1) hold dK^T and dV^T accumulators; gradient
+//                  wave KW + k owns key blocks 2*(k/2) and 2*(k/2) + 1 and the
+//                  d blocks of group k % 2 (D/64 of them); one item later they
+//                  read P and dS of their key blocks back and accumulate
+//                  dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read
+//                  transposed from the item's tiles, each transposed operand
+//                  feeding both key blocks' MFMAs.
 // Score wave k and gradient wave KW + k share a SIMD.  Each item takes two
 // barriers: before the first the score waves run their MFMAs while the
 // gradient waves fetch P and dS (both groups first issue their share of the
@@ -166,6 +172,10 @@ struct DkdvWs {
   char* smem;  // [slot][Q tile, dO tile], [score wave][P, dS images], [slot][lse2, dsum]
   const AttnArgs* a;
   int b, hk, k0, k_last, key, qt_lo, n_qt, n_items, wave, kb, lane, hf;
+  int kp, dg;  // gradient waves: key-block pair and d-block group they accumulate
+  // A gradient wave owns key blocks 2*kp, 2*kp + 1 and d blocks NDW*dg .. NDW*dg + NDW - 1.
+  static constexpr int NDW = D / 64;
+  int gtr[NDW][2];  // off.tr of this gradient wave's d blocks (set_grad_blocks)
   float c;
   SwzOffsets<D> off;
   // The score waves load the Q tiles and row statistics, the gradient waves
@@ -217,8 +227,29 @@ struct DkdvWs {
     }
   }
 
-  __device__ __forceinline__ char* img(int which) const {
-    return smem + L::OFF_PDS + (kb * 2 + which) * L::IMG + lane * 16;
+  // Gradient waves: key-block pair and d-block group of wave index gw in
+  // the group (d-block offsets picked with a select, so that the offset
+  // table keeps constant indices).
+  __device__ __forceinline__ void set_grad_blocks(int gw) {
+    kp = gw / 2;
+    dg = gw % 2;
+#pragma unroll
+    for (int dd = 0; dd < NDW; ++dd) {
+      gtr[dd][0] = dg ? off.tr[NDW + dd][0] : off.tr[dd][0];
+      gtr[dd][1] = dg ? off.tr[NDW + dd][1] : off.tr[dd][1];
+    }
+  }
+  // Transposed operand of this gradient wave's d block dd, 16-row step si.
+  __device__ __forceinline__ u32x4 gtr_operand(const char* tile, int si, int dd) const {
+    const char* t = tile + si * 16 * 2 * D;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + gtr[dd][0]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(t + gtr[dd][1]));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+  __device__ __forceinline__ char* img(int which) const { return img_of(kb, which); }
+  __device__ __forceinline__ char* img_of(int kbw, int which) const {
+    return smem + L::OFF_PDS + (kbw * 2 + which) * L::IMG + lane * 16;
   }
 
   // S = Q K^T and dP = dO V^T of one item, 16 d-columns (one step st) at a
@@ -258,31 +289,36 @@ struct DkdvWs {
     }
   }
 
-  // dV^T += dO^T P and dK^T += Q^T dS over the (16-query step si, 32-column
-  // block db) pairs of one item; the transposed operands of pair p + NB - 1
-  // are read while the MFMAs of pair p run.
-  __device__ __forceinline__ void grad_products(const char* Qs, const char* dOs, const u32x4 (&pf)[BMQ / 16],
-                                                const u32x4 (&dsf)[BMQ / 16], f32x16 (&dka)[D / 32],
+  // dV^T += dO^T P and dK^T += Q^T dS of one item for this gradient wave's
+  // two key blocks and NDW d blocks, over the (16-query step si, d block)
+  // pairs; each transposed operand feeds the MFMAs of both key blocks (the
+  // transposing LDS reads run at a quarter of the rate of plain 16-byte
+  // reads), and those of pair p + NB - 1 are read while the MFMAs of pair p run.
+  __device__ __forceinline__ void grad_products(const char* Qs, const char* dOs, const u32x4 (&pf)[2][BMQ / 16],
+                                                const u32x4 (&dsf)[2][BMQ / 16], f32x16 (&dka)[D / 32],
                                                 f32x16 (&dva)[D / 32]) {
-    constexpr int NDB = D / 32, NP = (BMQ / 16) * NDB, NB = 4;
+    constexpr int NP = (BMQ / 16) * NDW, NB = FA_DKDV_GRING;
     static_assert(NP >= NB, "pairs");
     u32x4 ao[NB], aq[NB];
 #pragma unroll
     for (int pr = 0; pr < NB - 1; ++pr) {
-      ao[pr] = off.tr_operand(dOs, pr / NDB, pr % NDB);
-      aq[pr] = off.tr_operand(Qs, pr / NDB, pr % NDB);
+      ao[pr] = gtr_operand(dOs, pr / NDW, pr % NDW);
+      aq[pr] = gtr_operand(Qs, pr / NDW, pr % NDW);
     }
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
       if (pr + NB - 1 < NP) {
         const int nx = pr + NB - 1;
-        ao[nx % NB] = off.tr_operand(dOs, nx / NDB, nx % NDB);
-        aq[nx % NB] = off.tr_operand(Qs, nx / NDB, nx % NDB);
+        ao[nx % NB] = gtr_operand(dOs, nx / NDW, nx % NDW);
+        aq[nx % NB] = gtr_operand(Qs, nx / NDW, nx % NDW);
       }
       __builtin_amdgcn_sched_barrier(0);
-      const int si = pr / NDB, db = pr % NDB;
-      dva[db] = T::mfma(ao[pr % NB], pf[si], dva[db]);
-      dka[db] = T::mfma(aq[pr % NB], dsf[si], dka[db]);
+      const int si = pr / NDW, dd = pr % NDW;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        dva[kk * NDW + dd] = T::mfma(ao[pr % NB], pf[kk][si], dva[kk * NDW + dd]);
+        dka[kk * NDW + dd] = T::mfma(aq[pr % NB], dsf[kk][si], dka[kk * NDW + dd]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -369,16 +405,19 @@ struct DkdvWs {
   // `pslot`).
   __device__ __forceinline__ void grad_step(int w, int pslot, int nslot, Cursor& nx, f32x16 (&dka)[D / 32],
                                             f32x16 (&dva)[D / 32]) {
-    u32x4 pf[BMQ / 16], dsf[BMQ / 16];
+    u32x4 pf[2][BMQ / 16], dsf[2][BMQ / 16];
     if (w + 1 < n_items) issue<false, true>(nx, nslot);
     nx.next(a->G);
     if (w >= 1) {
-      const char* pimg = img(0);
-      const char* dimg = img(1);
 #pragma unroll
-      for (int si = 0; si < BMQ / 16; ++si) {
-        pf[si] = *reinterpret_cast<const u32x4*>(pimg + si * 1024);
-        dsf[si] = *reinterpret_cast<const u32x4*>(dimg + si * 1024);
+      for (int kk = 0; kk < 2; ++kk) {
+        const char* pimg = img_of(2 * kp + kk, 0);
+        const char* dimg = img_of(2 * kp + kk, 1);
+#pragma unroll
+        for (int si = 0; si < BMQ / 16; ++si) {
+          pf[kk][si] = *reinterpret_cast<const u32x4*>(pimg + si * 1024);
+          dsf[kk][si] = *reinterpret_cast<const u32x4*>(dimg + si * 1024);
+        }
       }
     }
     wait_all_loads();  // this wave's share of item w + 1 has landed (before any transposing read)
@@ -452,7 +491,7 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
   x.kb = wave % L::KW;
   x.lane = lane;
   x.hf = lane >> 5;
-  x.key = x.k0 + x.kb * 32 + (lane & 31);  // this lane's key (accumulator column)
+  x.key = x.k0 + x.kb * 32 + (lane & 31);  // this lane's key (accumulator column) in a score wave
   x.c = a.scale_log2;
   x.k_last = min(x.k0 + L::BNK, a.Nk) - 1;
   const int i_lo = query_lo(a, x.k0), i_hi = query_hi(a, x.k_last);
@@ -460,6 +499,7 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
   x.n_qt = (i_hi >= i_lo) ? i_hi / BMQ - x.qt_lo + 1 : 0;
   x.n_items = x.n_qt * a.G;  // (query tile, query head of the group) pairs
   x.off.init(lane);
+  x.set_grad_blocks(wave % L::KW);
   x.qd.init(x.kb, lane, a.q_sn, a.D / 8);
   x.dd.init(x.kb, lane, a.o_sn, a.D / 8);
 
@@ -475,23 +515,35 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
   f32x16 dka[D / 32], dva[D / 32];
   x.grad_loop(dka, dva);
 
-  // Store dK = scale * dK and dV: lane holds d rows 32*db + 8*g4 + 4*hf + 0..3.
-  if (x.key < a.Nk) {
-    uint16_t* dkp = static_cast<uint16_t*>(a.dk) + x.b * a.k_sb + x.hk * a.k_sh + (int64_t)x.key * a.k_sn;
-    uint16_t* dvp = static_cast<uint16_t*>(a.dv) + x.b * a.v_sb + x.hk * a.v_sh + (int64_t)x.key * a.v_sn;
-    const float sc = a.scale;
-    const int hf = x.hf;
+  // Store dK = scale * dK and dV: block kk * NDW + dd holds key block
+  // 2*kp + kk (lane's key in it: lane % 32) and d rows
+  // 32*(NDW*dg + dd) + 8*g4 + 4*hf + 0..3.
+  constexpr int NDW = DkdvWs<T, D, BMQ, MOD>::NDW;
+  const float sc = a.scale;
+  const int nk = a.Nk, hd = a.D;
+  const int64_t k_sn = a.k_sn, v_sn = a.v_sn;
+  uint16_t* const dkb = static_cast<uint16_t*>(a.dk) + x.b * a.k_sb + x.hk * a.k_sh;
+  uint16_t* const dvb = static_cast<uint16_t*>(a.dv) + x.b * a.v_sb + x.hk * a.v_sh;
+  const int key0 = x.k0 + 2 * x.kp * 32 + (lane & 31);
+  const int dcol0 = 32 * NDW * x.dg + 4 * x.hf;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+  for (int kk = 0; kk < 2; ++kk) {
+    const int key = key0 + 32 * kk;
+    uint16_t* dkp = dkb + (int64_t)key * k_sn;
+    uint16_t* dvp = dvb + (int64_t)key * v_sn;
+#pragma unroll
+    for (int dd = 0; dd < NDW; ++dd) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * db + 8 * g4 + 4 * hf;
-        if (d0 >= a.D) continue;
-        *reinterpret_cast<u32x2*>(dkp + d0) =
-            u32x2{T::pack(dka[db][4 * g4] * sc, dka[db][4 * g4 + 1] * sc),
-                  T::pack(dka[db][4 * g4 + 2] * sc, dka[db][4 * g4 + 3] * sc)};
-        *reinterpret_cast<u32x2*>(dvp + d0) =
-            u32x2{T::pack(dva[db][4 * g4], dva[db][4 * g4 + 1]), T::pack(dva[db][4 * g4 + 2], dva[db][4 * g4 + 3])};
+        const int d0 = dcol0 + 32 * dd + 8 * g4;
+        const f32x16& ka = dka[kk * NDW + dd];
+        const f32x16& va = dva[kk * NDW + dd];
+        if (key < nk && d0 < hd) {
+          *reinterpret_cast<u32x2*>(dkp + d0) = u32x2{T::pack(ka[4 * g4] * sc, ka[4 * g4 + 1] * sc),
+                                                      T::pack(ka[4 * g4 + 2] * sc, ka[4 * g4 + 3] * sc)};
+          *reinterpret_cast<u32x2*>(dvp + d0) =
+              u32x2{T::pack(va[4 * g4], va[4 * g4 + 1]), T::pack(va[4 * g4 + 2], va[4 * g4 + 3])};
+        }
       }
     }
   }
