@@ -91,8 +91,8 @@ def flops(w):
 # built from the sources whose SHA-256 is recorded here and are reported as
 # null for any other source.
 DKDV_TRAFFIC = {
-    "sources_sha256": "f3dd78c97488e5da36e667ea15df8a60d564fff01042fc54de6bcc8db35f4b43",
-    "bytes_per_launch": 2081126083,
+    "sources_sha256": "7f3b73787ce81867f0667786435379fad0ffedc94a32a13d1a0aecff16b962c8",
+    "bytes_per_launch": 2054225107,
 }
 
 
