@@ -91,8 +91,8 @@ def flops(w):
 # built from the sources whose SHA-256 is recorded here and are reported as
 # null for any other source.
 DKDV_TRAFFIC = {
-    "sources_sha256": "7f3b73787ce81867f0667786435379fad0ffedc94a32a13d1a0aecff16b962c8",
-    "bytes_per_launch": 2054225107,
+    "sources_sha256": "836eb6d227303a68b9dabdbdde13718ce6a5461c851bf9a3954771b3221151df",
+    "bytes_per_launch": 1919901894,
 }
 
 

@@ -143,8 +143,8 @@ hipError_t launch_bwd_preprocess(const AttnArgs& a, hipStream_t stream) {
 //                  feeding both key blocks' MFMAs.
 // Score wave k and gradient wave KW + k share a SIMD.  Each item takes two
 // barriers: before the first the score waves run their MFMAs while the
-// gradient waves fetch P and dS (both groups first issue their share of the
-// next item's tile loads); after it the gradient waves run their MFMAs while
+// gradient waves fetch P and dS and issue the next item's tile loads; after
+// it the gradient waves run their MFMAs while
 // the score waves do the exponentials.  So the matrix core of every SIMD
 // always has one wave feeding it, and the vector work hides behind it.
 // Q/dO tiles rotate through three LDS slots (the item being scored, the item
@@ -178,13 +178,14 @@ struct DkdvWs {
   int gtr[NDW][2];  // off.tr of this gradient wave's d blocks (set_grad_blocks)
   float c;
   SwzOffsets<D> off;
-  // The score waves load the Q tiles and row statistics, the gradient waves
-  // the dO tiles, both at the start of an item (a wave's loads issue slowly
-  // while another wave of its SIMD streams MFMAs, and neither group runs
-  // MFMAs there yet).  A wave whose transposing LDS reads follow its own
-  // direct-to-LDS loads in program order is made to wait for those loads by
-  // the compiler, even where they cannot overlap; the gradient waves wait for
-  // theirs before the item's first barrier anyway.
+  // The gradient waves load the next item's Q and dO tiles and row
+  // statistics at the start of an item, while they have no MFMAs to run and
+  // the score waves start their products at once (a CU's tile loads pass its
+  // address unit at a limited rate, so a wave that issues them waits).  A
+  // wave whose transposing LDS reads follow its own direct-to-LDS loads in
+  // program order is made to wait for those loads by the compiler, even where
+  // they cannot overlap; the gradient waves wait for theirs before the item's
+  // first barrier anyway.
   DmaTile<D, BMQ, L::KW> qd, dd;
 
   // Work items run over query tiles from the last one down, with the heads of
@@ -324,13 +325,11 @@ struct DkdvWs {
   }
 
   // One item of a score wave: item w (if w < n_items) sits in slot `slot`;
-  // item w + 1 (cursor nx) is loaded into slot `nslot` meanwhile.
+  // the gradient waves load item w + 1 (cursor nx) into slot `nslot` meanwhile.
   __device__ __forceinline__ void score_step(int w, int slot, int nslot, Cursor& cu, Cursor& nx,
                                              const u32x4 (&kf)[D / 16], const u32x4 (&vf)[D / 16]) {
     // [qb][r] is query i0 + 32*qb + 8*(r/4) + 4*hf + r%4.
     f32x16 s[BMQ / 32], dp[BMQ / 32];
-    // The next item's Q tile goes out before this item's products.
-    if (w + 1 < n_items) issue<true, false>(nx, nslot);
     if (w < n_items) score_products(slot_tiles(slot), slot_tiles(slot) + L::TILE * 2, kf, vf, s, dp);
     lds_barrier();  // the gradient waves have taken the previous item's P and dS
     if (w < n_items) {
@@ -400,13 +399,13 @@ struct DkdvWs {
     nx.next(a->G);
   }
 
-  // One item of a gradient wave: load the dO tile of item w + 1 (cursor nx)
-  // into slot nslot, which held item w - 2; accumulate item w - 1 (slot
-  // `pslot`).
+  // One item of a gradient wave: load the Q and dO tiles and statistics of
+  // item w + 1 (cursor nx) into slot nslot, which held item w - 2; accumulate
+  // item w - 1 (slot `pslot`).
   __device__ __forceinline__ void grad_step(int w, int pslot, int nslot, Cursor& nx, f32x16 (&dka)[D / 32],
                                             f32x16 (&dva)[D / 32]) {
     u32x4 pf[2][BMQ / 16], dsf[2][BMQ / 16];
-    if (w + 1 < n_items) issue<false, true>(nx, nslot);
+    if (w + 1 < n_items) issue<true, true>(nx, nslot);
     nx.next(a->G);
     if (w >= 1) {
 #pragma unroll
