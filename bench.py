@@ -91,8 +91,8 @@ def flops(w):
 # built from the sources whose SHA-256 is recorded here and are reported as
 # null for any other source.
 DKDV_TRAFFIC = {
-    "sources_sha256": "836eb6d227303a68b9dabdbdde13718ce6a5461c851bf9a3954771b3221151df",
-    "bytes_per_launch": 1919901894,
+    "sources_sha256": "95ba2e19879ee22bea89f17d14b6938169435cacf99ed1a43f58b3ba405c4795",
+    "bytes_per_launch": 1937298807,
 }
 
 

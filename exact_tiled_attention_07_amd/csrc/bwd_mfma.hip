@@ -564,7 +564,12 @@ struct DqCtx {
   u32x4 qf[D / 16], df[D / 16];
   f32x16 dqa[D / 32];
   SwzOffsets<D> off;
-  DmaTile<D, BN, NW> kd, vd;
+  // Waves NW - NLW .. NW - 1 (one of the two waves of each SIMD) issue the
+  // K/V tile loads while the other half start their products at once: a
+  // CU's tile loads pass its address unit at a limited rate, so a wave that
+  // issues them waits.
+  static constexpr int NLW = NW / 2;
+  DmaTile<D, BN, NLW> kd, vd;
 
   template <int BUF>
   __device__ __forceinline__ void step(int t) {
@@ -572,8 +577,10 @@ struct DqCtx {
     const char* Vs = Ks + TILE * 2;
     const int j0 = t * BN;
     if (t < t_hi) {
-      kd.issue(Kp, k_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE, wave);
-      vd.issue(Vp, v_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE + TILE, wave);
+      if (wave >= NW - NLW) {
+        kd.issue(Kp, k_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE, wave - (NW - NLW));
+        vd.issue(Vp, v_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE + TILE, wave - (NW - NLW));
+      }
     }
     // S^T = K Q^T and dP^T = V dO^T; element [kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
     // Operand o: step st = o / (2 * BN/32), key block kb, K (even o) or V (odd o)
@@ -724,12 +731,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) x.dqa[db] = f32x16{};
   x.off.init(lane);
-  x.kd.init(wave, lane, a.k_sn, a.D / 8);
-  x.vd.init(wave, lane, a.v_sn, a.D / 8);
+  x.kd.init(max(wave - (NW - Ctx::NLW), 0), lane, a.k_sn, a.D / 8);
+  x.vd.init(max(wave - (NW - Ctx::NLW), 0), lane, a.v_sn, a.D / 8);
 
   if (t_lo <= x.t_hi) {
-    x.kd.issue(x.Kp, a.k_sn, t_lo * BN, a.Nk, smem, wave);
-    x.vd.issue(x.Vp, a.v_sn, t_lo * BN, a.Nk, smem + Ctx::TILE, wave);
+    if (wave >= NW - Ctx::NLW) {
+      x.kd.issue(x.Kp, a.k_sn, t_lo * BN, a.Nk, smem, wave - (NW - Ctx::NLW));
+      x.vd.issue(x.Vp, a.v_sn, t_lo * BN, a.Nk, smem + Ctx::TILE, wave - (NW - Ctx::NLW));
+    }
     wait_all_loads();
   }
   __syncthreads();
