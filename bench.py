@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--decode-calls", type=int, default=200, help="timed fa_fwd_kvcache calls (0: skip)")
     ap.add_argument("--next-rows-steps", type=int, default=10,
                     help="timed steps of the packed-batch and score-modifier legs (0: skip)")
+    ap.add_argument("--config-calls", type=int, default=10,
+                    help="timed calls per repeat (5 repeats) of each named workload's fwd and bwd (0: skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="instead of the benchmark, run a plain device copy of 512 MiB (read 512 MiB, "
                          "write 512 MiB) 5 times: the known-size reference for HBM byte counters")
@@ -359,6 +361,76 @@ def next_rows_leg(steps):
     return out
 
 
+def configs_leg(calls, repeats=5):
+    """fa_fwd alone and fa_bwd alone (on the forward's outputs) on every named
+    workload at its full size, inputs resident in HBM, outputs preallocated,
+    no cache flush between calls: 3 warm-up calls, then `repeats` runs of
+    `calls` calls between two events on the launch stream; the median run's
+    average per call.  fp16/bf16 rates are set against the dense MFMA peak;
+    the fp32 path runs on the vector ALU and is not rated."""
+    import statistics
+
+    import torch
+
+    import exact_tiled_attention_07_amd as fa
+    from exact_tiled_attention_07_amd.workloads import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    out = {"calls_per_repeat": calls, "repeats": repeats, "statistic": "median of repeats",
+           "cache": "not flushed between calls"}
+    for name, w in WORKLOADS.items():
+        q, k, v, do = (t.to(dev) for t in make_inputs(w))
+        kw = dict(causal=w.causal, window_size=w.window)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.batch, w.nheads_q, w.seqlen), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.bwd_workspace_size(fa.make_params(q, k, v, o, **kw)), dtype=torch.uint8, device=dev)
+
+        def fwd():
+            fa.fwd(q, k, v, out=o, lse=lse, **kw)
+
+        def bwd():
+            fa.bwd(do, q, k, v, o, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+
+        def time_it(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            runs = []
+            for _ in range(repeats):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(calls):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                runs.append(e0.elapsed_time(e1) / calls)
+            return statistics.median(runs)
+
+        f_fwd, f_bwd = flops(w)
+        rated = w.dtype != "fp32"
+        entry = {"dtype": w.dtype, "shape": [w.batch, w.seqlen, w.nheads_q, w.nheads_kv, w.headdim],
+                 "causal": w.causal, "window": list(w.window), "sigma": w.sigma}
+        fm = time_it(fwd)
+        entry.update(fwd_ms=round(fm, 4), fwd_tflops=round(f_fwd / (fm * 1e-3) / 1e12, 2))
+        if rated:
+            entry["fwd_frac"] = round(f_fwd / (fm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        if w.backward:
+            fwd()
+            bm = time_it(bwd)
+            entry.update(bwd_ms=round(bm, 4), bwd_tflops=round(f_bwd / (bm * 1e-3) / 1e12, 2))
+            tf = (f_fwd + f_bwd) / ((fm + bm) * 1e-3) / 1e12
+            entry["fwd_bwd_tflops"] = round(tf, 2)
+            if rated:
+                entry["bwd_frac"] = round(f_bwd / (bm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                entry["fwd_bwd_frac"] = round(tf / PEAK_BF16_TFLOPS, 4)
+        assert torch.isfinite(o).all()
+        out[name] = entry
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+    return out
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -468,6 +540,8 @@ def main():
         out["decode"] = decode_leg(args.decode_calls)
     if args.next_rows_steps > 0:
         out["next_rows"] = next_rows_leg(args.next_rows_steps)
+    if args.config_calls > 0:
+        out["configs"] = configs_leg(args.config_calls)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q_c, k_c, v_c, do_c, args.cpu_seconds)
     print(json.dumps(out), flush=True)

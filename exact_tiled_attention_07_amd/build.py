@@ -26,7 +26,7 @@ HEADERS = ["common.hpp", "tile_io.hpp", "launch.hpp"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Werror",
     # Packed-fp32 VALU forms stay off: hipcc -O3 would otherwise fuse pairs of
     # fp32 adds/muls/FMAs into them.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

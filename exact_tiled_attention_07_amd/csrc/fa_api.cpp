@@ -52,8 +52,13 @@ fa_status check_params(const fa_params* p) {
   if (p->nheads_q % p->nheads_kv != 0)
     return fail(FA_ERR_INVALID_ARG, "nheads_q (%lld) must be a multiple of nheads_kv (%lld)",
                 (long long)p->nheads_q, (long long)p->nheads_kv);
-  if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16)
-    return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)p->dtype);
+  // A C caller can store any int in the enum field; reading it as the C++
+  // enum before it is known to be valid is undefined, so take its raw bits.
+  static_assert(sizeof(p->dtype) == sizeof(int32_t), "fa_dtype is a 32-bit enum");
+  int32_t dtype_raw;
+  std::memcpy(&dtype_raw, &p->dtype, sizeof dtype_raw);
+  if (dtype_raw != FA_F32 && dtype_raw != FA_F16 && dtype_raw != FA_BF16)
+    return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype_raw);
   if (!(std::isfinite(p->scale) && p->scale > 0.f))
     return fail(FA_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (p->causal != 0 && p->causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
@@ -94,6 +99,14 @@ fa_status check_params(const fa_params* p) {
         return fail(FA_ERR_UNSUPPORTED, "%s_strides[%d]=%lld is not a multiple of 16 bytes", names[t], i,
                     (long long)s);
     }
+  }
+  // Rows of one head must not overlap: the tile loads bound a tile by
+  // rows * row stride bytes, and outputs written through overlapping rows race.
+  const int64_t rows[4] = {p->seqlen_q, p->seqlen_k, p->seqlen_k, p->seqlen_q};
+  for (int t = 0; t < 4; ++t) {
+    if (rows[t] > 1 && strides[t][1] < p->headdim)
+      return fail(FA_ERR_UNSUPPORTED, "%s_strides[1]=%lld is below headdim (%lld): rows would overlap", names[t],
+                  (long long)strides[t][1], (long long)p->headdim);
   }
   return FA_OK;
 }
@@ -511,6 +524,14 @@ fa_status run_kvcache(const fa_kvcache_params* params, int32_t page_size, int64_
   if ((s = check_ptr(lse, "lse", true)) != FA_OK) return s;
   if ((s = check_ptr(k_new, "k_new", k_new != nullptr)) != FA_OK) return s;
   if ((s = check_ptr(v_new, "v_new", v_new != nullptr)) != FA_OK) return s;
+  if (k_new && p->seqlen_q > 1) {  // new rows must not overlap (as in check_params)
+    const int64_t* ns[2] = {params->knew_strides, params->vnew_strides};
+    const char* nn[2] = {"knew", "vnew"};
+    for (int t = 0; t < 2; ++t)
+      if (ns[t][1] < p->headdim)
+        return fail(FA_ERR_UNSUPPORTED, "%s_strides[1]=%lld is below headdim (%lld): rows would overlap", nn[t],
+                    (long long)ns[t][1], (long long)p->headdim);
+  }
   if (!cache_seqlens) return fail(FA_ERR_INVALID_ARG, "cache_seqlens is NULL");
   if (page_size != 0) {
     if (!block_table) return fail(FA_ERR_INVALID_ARG, "block_table is NULL");
@@ -596,7 +617,11 @@ fa_status fa_fwd_kvcache_paged(const fa_kvcache_params* params, int32_t page_siz
 }
 
 const char* fa_status_string(fa_status status) {
-  switch (status) {
+  // Any int may arrive from C; take the raw bits (see check_params).
+  int32_t raw;
+  static_assert(sizeof status == sizeof raw, "fa_status is a 32-bit enum");
+  std::memcpy(&raw, &status, sizeof raw);
+  switch (raw) {
     case FA_OK: return "FA_OK";
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";

@@ -86,15 +86,41 @@ def make_inputs(w: Workload, seed=None, batch=None, seqlen=None):
     return q, k, v, do
 
 
-def random_qkv(shape_q, shape_kv, dtype, seed, sigma=1.0):
-    """Same recipe for an arbitrary shape (test sweeps)."""
+def random_qkv(shape_q, shape_kv, dtype, seed, sigma=1.0, sigma_v=None):
+    """Same recipe for an arbitrary shape (test sweeps); ``sigma_v`` (default
+    ``sigma``) sets the std of v alone."""
     g = torch.Generator("cpu").manual_seed(seed)
     dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    sv = sigma if sigma_v is None else sigma_v
     q = (torch.randn(shape_q, generator=g, dtype=torch.float32) * sigma).to(dt)
     k = (torch.randn(shape_kv, generator=g, dtype=torch.float32) * sigma).to(dt)
-    v = (torch.randn(shape_kv, generator=g, dtype=torch.float32) * sigma).to(dt)
+    v = (torch.randn(shape_kv, generator=g, dtype=torch.float32) * sv).to(dt)
     do = torch.randn(shape_q, generator=g, dtype=torch.float32).to(dt)
     return q, k, v, do
+
+
+def monotone_key_qkv(shape_q, shape_kv, dtype, seed, rise_per_key, q_gain=1.0):
+    """Inputs whose scaled scores climb along the keys: k_j = (j / N) * c * u +
+    0.1 * noise and q_i = q_gain * u + 0.5 * noise, with u a random N(0, 1)
+    direction, so that q_i . u is about q_gain * headdim > 0 for every query.
+    The scaled score q_i . k_j / sqrt(headdim) then grows by about
+    ``rise_per_key`` (natural-log units) from one key to the next
+    (c = rise_per_key * N / (q_gain * sqrt(headdim))), so a running row maximum
+    taken tile by tile rises on every tile; q_gain moves magnitude from the
+    keys to the queries.  v and dO are N(0, 1).  All drawn from one seeded CPU
+    generator, then rounded to dtype."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    dt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    b, n, hq, d = shape_q
+    _, nk, hkv, _ = shape_kv
+    u = torch.randn((d,), generator=g, dtype=torch.float32)
+    c = rise_per_key * nk / (q_gain * d ** 0.5)
+    ramp = (torch.arange(nk, dtype=torch.float32) / nk)[None, :, None, None]
+    k = ramp * c * u + 0.1 * torch.randn(shape_kv, generator=g, dtype=torch.float32)
+    q = q_gain * u + 0.5 * torch.randn(shape_q, generator=g, dtype=torch.float32)
+    v = torch.randn(shape_kv, generator=g, dtype=torch.float32)
+    do = torch.randn(shape_q, generator=g, dtype=torch.float32)
+    return q.to(dt), k.to(dt), v.to(dt), do.to(dt)
 
 
 @dataclass(frozen=True)

@@ -1,12 +1,15 @@
 """Helpers shared by the GPU parity tests: run the HIP path through the C ABI
 binding, run the float64 oracle on the same CPU inputs, and compare."""
 
+import json
+import os
+
 import numpy as np
 import torch
 
 import exact_tiled_attention_07_amd as fa
 import oracle
-from compare import within
+from compare import describe, within
 
 # Max-abs tolerances of the HIP path against the float64 oracle: O and LSE
 # use the first, dQ/dK/dV twice it.
@@ -32,11 +35,22 @@ def max_err(got, ref):
 DTYPE_NAME = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}
 
 
+def record_errors(case, errors):
+    """Appends {case, output: statistics} as one JSON line to the file named by
+    FA_PARITY_LOG, if set (the literal max-abs errors of the full-size runs)."""
+    path = os.environ.get("FA_PARITY_LOG")
+    if not path:
+        return
+    with open(path, "a") as f:
+        f.write(json.dumps({"case": case, **{k: {kk: (None if vv == float("inf") else vv) for kk, vv in v.items()}
+                                             for k, v in errors.items()}}) + "\n")
+
+
 def assert_close(got, ref, tol, what):
     """Oracle comparison rule of compare.py for a GPU tensor against a float64 array."""
     ok, info = within(f64(got), ref, DTYPE_NAME[got.dtype], tol)
-    assert ok, f"{what}: raw {info['raw']:.3e}, excess over output rounding {info['excess']:.3e}, " \
-               f"raw where |ref|<4 {info['raw_small']:.3e}; tolerance {tol:.1e}"
+    info = dict(info, tol=tol)
+    assert ok, f"{what}: {describe(info, tol)}"
     return info
 
 

@@ -34,7 +34,8 @@ def header_functions():
 
 def test_header_declares_expected_entry_points():
     assert header_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd_kvcache", "fa_fwd_kvcache_paged",
+        ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd_kvcache",
+         "fa_fwd_kvcache_paged",
          "fa_fwd_kvcache_workspace_size", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
          "fa_status_string", "fa_last_error", "fa_version"])
 
@@ -152,6 +153,10 @@ UNSUPPORTED = [
     ("fp32 headdim 132", dict(dtype=0, headdim=132)),
     ("stride not 16 bytes", dict(k_strides=(64 * 2 * 64, 2 * 64, 68))),
     ("negative stride", dict(q_strides=(-16, 256, 64))),
+    ("zero sequence stride (expanded k)", dict(k_strides=(64 * 2 * 64, 0, 64))),
+    ("sequence stride below headdim (q rows overlap)", dict(q_strides=(64 * 4 * 64, 32, 64))),
+    ("sequence stride below headdim (o rows overlap)", dict(o_strides=(64 * 4 * 64, 56, 64))),
+    ("sequence stride below headdim (v rows overlap)", dict(v_strides=(64 * 2 * 64, 8, 64))),
     ("huge seqlen", dict(seqlen_q=1 << 31, seqlen_k=1 << 31)),
     ("misaligned alibi slopes", dict(alibi_slopes=0x1002)),
 ]
@@ -317,6 +322,11 @@ def test_kvcache_specific_validation(lib):
     assert call_kv(lib, kv_params(num_splits=-1)) == N.FA_ERR_INVALID_ARG
     assert b"num_splits" in lib.fa_last_error()
     assert call_kv(lib, kv_params(reserved=1)) == N.FA_ERR_INVALID_ARG
+    # without new rows their strides are not looked at (here: zeros, Nq = 4)
+    nq4 = dict(seqlen_q=4, q_strides=(4 * 4 * 64, 4 * 64, 64), o_strides=(4 * 4 * 64, 4 * 64, 64),
+               knew_strides=(0, 0, 0), vnew_strides=(0, 0, 0))
+    assert call_kv(lib, kv_params(**nq4), kn=None, vn=None) != N.FA_ERR_UNSUPPORTED
+    assert call_kv(lib, kv_params(**nq4)) == N.FA_ERR_UNSUPPORTED
     assert call_kv(lib, kv_params(), kn=None) == N.FA_ERR_INVALID_ARG       # one of the pair
     assert b"k_new" in lib.fa_last_error()
     assert call_kv(lib, kv_params(), lens=None) == N.FA_ERR_INVALID_ARG
@@ -333,14 +343,20 @@ def test_kvcache_specific_validation(lib):
     assert lib.fa_fwd_kvcache_workspace_size(ctypes.byref(kv_params()), None) == N.FA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("name,kw", [
+KV_UNSUPPORTED = [
     ("fp32", dict(dtype=0)),
     ("headdim 144", dict(headdim=144, q_strides=(4 * 144, 4 * 144, 144), o_strides=(4 * 144, 4 * 144, 144),
                          k_strides=(256 * 2 * 144, 2 * 144, 144), v_strides=(256 * 2 * 144, 2 * 144, 144),
                          knew_strides=(2 * 144, 2 * 144, 144), vnew_strides=(2 * 144, 2 * 144, 144))),
     ("new-row stride not 16 bytes", dict(knew_strides=(2 * 64, 2 * 64, 60))),
     ("negative new-row stride", dict(vnew_strides=(-128, 128, 64))),
-])
+    ("overlapping new rows", dict(seqlen_q=4, q_strides=(4 * 4 * 64, 4 * 64, 64), o_strides=(4 * 4 * 64, 4 * 64, 64),
+                                  knew_strides=(4 * 2 * 64, 32, 64), vnew_strides=(4 * 2 * 64, 2 * 64, 64))),
+    ("overlapping cache rows", dict(k_strides=(256 * 2 * 64, 0, 64))),
+]
+
+
+@pytest.mark.parametrize("name,kw", KV_UNSUPPORTED, ids=[x[0] for x in KV_UNSUPPORTED])
 def test_kvcache_unsupported_arguments(lib, name, kw):
     assert call_kv(lib, kv_params(**kw)) == N.FA_ERR_UNSUPPORTED
 

@@ -19,7 +19,7 @@ if not torch.cuda.is_available():  # collected on CPU machines, never run there
 import exact_tiled_attention_07_amd as fa  # noqa: E402
 import oracle  # noqa: E402
 from exact_tiled_attention_07_amd.workloads import WORKLOADS, make_inputs, random_qkv  # noqa: E402
-from gpu_util import TOL, assert_close, check_bwd, check_fwd, f64, gpu_bwd, gpu_fwd, max_err  # noqa: E402
+from gpu_util import TOL, assert_close, check_bwd, check_fwd, f64, gpu_bwd, gpu_fwd, max_err, record_errors  # noqa: E402,E501
 
 DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
 MASKS = [
@@ -95,14 +95,21 @@ def test_unequal_lengths(dtype, nq, nk, mask):
 
 @pytest.mark.parametrize("dtype,scales", [("fp32", (0.02, 0.3)), ("fp16", (0.02, 0.15)), ("bf16", (0.02, 0.15))])
 def test_scale_parameter(dtype, scales):
-    # 16-bit inputs stop at 1.7x the default 1/sqrt(128): dS is rounded to the
-    # input type before the dQ/dK products, and at scale 0.3 (score std ~3.4)
-    # that rounding alone gives dQ errors of 1.3x the gradient bar (0.040 for
-    # bf16, 0.0053 for fp16).
     q, k, v, do = random_qkv((2, 100, 4, 128), (2, 100, 2, 128), dtype, seed=5)
     for s in scales:
         check_fwd(q, k, v, causal=True, scale=s)
         check_bwd(q, k, v, do, causal=True, scale=s)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.xfail(strict=True, reason="16-bit dS: the kernels round dS = P * (dP - D) to the input type before "
+                                       "the dQ and dK products; at scale 0.3 (score std 3.4) that rounding alone "
+                                       "puts dQ at about 1.3x the gradient bound")
+def test_scale_parameter_large_16bit(dtype):
+    # The forward meets its bound at this scale; the gradients do not.
+    q, k, v, do = random_qkv((2, 100, 4, 128), (2, 100, 2, 128), dtype, seed=5)
+    check_fwd(q, k, v, causal=True, scale=0.3)
+    check_bwd(q, k, v, do, causal=True, scale=0.3)
 
 
 # ---------------------------------------------------------------------------
@@ -256,6 +263,13 @@ def _head_slices(w, q, k, v, do, b, g):
             f64(do[b:b + 1, :, sl]), sl)
 
 
+def _sample_rows(n):
+    """Rows checked on every head at full size: the first, both sides of a
+    256-query workgroup boundary, a row inside a diagonal tile in the middle,
+    and the last."""
+    return sorted({0, min(255, n - 1), min(256, n - 1), min(n // 2 + 77, n - 1), n - 1})
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workload_full_size(name):
     w = WORKLOADS[name]
@@ -269,8 +283,11 @@ def test_workload_full_size(name):
     tol = TOL[DT[w.dtype]]
     ow = dict(causal=w.causal, window=w.window)
     small = w.batch * w.nheads_q * w.seqlen <= 16 * 1024 * 2
+    # Whole (batch, kv head) groups: all of them for small workloads, else two on
+    # different batch entries and XCDs (unit b * Hkv + g runs on XCD unit % 8).
     groups = [(b, g) for b in range(w.batch) for g in range(w.nheads_kv)] if small else \
-        [(w.batch - 1, w.nheads_kv - 1)] + ([(0, 0)] if not w.backward else [])
+        sorted({(w.batch - 1, w.nheads_kv - 1), (0, 0)})
+    errors = {}
     for b, g in groups:
         qs, ks, vs, dos, sl = _head_slices(w, q, k, v, do, b, g)
         _note(f"  oracle group b={b} g={g}")
@@ -282,7 +299,26 @@ def test_workload_full_size(name):
             info["dq"] = assert_close(dq[b:b + 1, :, sl], rq, 2 * tol, "dQ")
             info["dk"] = assert_close(dk[b:b + 1, :, g:g + 1], rk, 2 * tol, "dK")
             info["dv"] = assert_close(dv[b:b + 1, :, g:g + 1], rv, 2 * tol, "dV")
-        _note("  " + ", ".join(f"{n}: raw {e['raw']:.2e} excess {e['excess']:.2e}" for n, e in info.items()))
+        _note("  " + ", ".join(f"{n}: max-abs {e['raw']:.2e} at |ref| {e['raw_ref']:.3g}" for n, e in info.items()))
+        for n, e in info.items():
+            if n not in errors or e["raw"] > errors[n]["raw"]:
+                errors[n] = e
+    if not small:
+        # Every (batch, query head) on sampled rows, one row at a time in the oracle.
+        rows = _sample_rows(w.seqlen)
+        qf, kf, vf = f64(q), f64(k), f64(v)
+        o_got = f64(o)[:, rows].transpose(0, 2, 1, 3)  # (B, Hq, R, d)
+        l_got = f64(lse)[:, :, rows]
+        o_ref = np.empty_like(o_got)
+        l_ref = np.empty_like(l_got)
+        for b in range(w.batch):
+            for h in range(w.nheads_q):
+                o_ref[b, h], l_ref[b, h] = oracle.attention_fwd_rows(qf, kf, vf, b, h, rows, **ow)
+        _note(f"  rows {rows} of all {w.batch * w.nheads_q} heads")
+        for n, got, ref in (("o_rows", o_got, o_ref), ("lse_rows", l_got, l_ref)):
+            e = assert_close(torch.from_numpy(got).to(DT[w.dtype] if n == "o_rows" else torch.float32), ref, tol, n)
+            errors[n] = e
+    record_errors(f"workload_{name}", errors)
     # Properties of the whole output (every head, not only the sampled ones).
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
     if w.backward:
