@@ -16,7 +16,7 @@ Python binding: torch provides device memory and streams only.
 from ._native import (  # noqa: F401
     FA_BF16, FA_BWD_DKDV, FA_BWD_DQ, FA_BWD_PREPARE, FA_ERR_HIP, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED,
     FA_F16, FA_F32, FA_OK, SIGNATURES,
-    FaError, FaKvParams, FaParams, FaVarlenParams, attention, attention_qkvpacked, attention_varlen, bwd,
+    FaError, FaKvParams, FaParams, FaVarlenParams, attention, attention_qkvpacked, attention_varlen, bwd, bwd_noalloc,
     bwd_varlen, bwd_varlen_workspace_size, bwd_workspace_size, fwd, fwd_kvcache, fwd_kvcache_paged, fwd_qkvpacked,
     fwd_varlen,
     kvcache_workspace_size, library_path, load_library, make_kv_params, make_params, make_varlen_params, version,

@@ -76,6 +76,7 @@ SIGNATURES = {
     "fa_bwd": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
     "fa_bwd_stage": (ctypes.c_int, [_P, ctypes.c_int, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t,
                                     _V]),
+    "fa_bwd_noalloc": (ctypes.c_int, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V]),
     "fa_fwd_varlen": (ctypes.c_int, [_PV, _V, _V, _V, _V, _V, _V, _V, _V]),
     "fa_bwd_varlen_workspace_size": (ctypes.c_int, [_PV, ctypes.POINTER(ctypes.c_size_t)]),
     "fa_bwd_varlen": (ctypes.c_int, [_PV, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, ctypes.c_size_t, _V]),
@@ -266,6 +267,33 @@ def bwd(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1), scale=No
             _check(lib.fa_bwd(ctypes.byref(p), *ptrs))
         else:
             _check(lib.fa_bwd_stage(ctypes.byref(p), int(stage), *ptrs))
+    return dq, dk, dv
+
+
+def bwd_noalloc(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1), scale=None, dq=None, dk=None,
+                dv=None, alibi_slopes=None, softcap=0.0):
+    """fa_bwd_noalloc: the backward of :func:`bwd` with the row statistics in
+    the library's static per-GPU scratch instead of a workspace.  The library
+    allocates nothing; gradient buffers not passed in are allocated here by
+    torch, as in :func:`bwd`."""
+    _require_gpu(dout, q, k, v, out, lse)
+    lib = load_library()
+    if dout.shape != q.shape or dout.dtype != q.dtype or dout.stride() != out.stride():
+        raise ValueError("dout must have the shape, dtype and strides of out")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[0], q.shape[2], q.shape[1]) \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (batch, nheads_q, seqlen_q) tensor")
+    p = make_params(q, k, v, out, causal=causal, window_size=window_size, scale=scale, alibi_slopes=alibi_slopes,
+                    softcap=softcap)
+    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device) if dv is None else dv
+    for g, ref in ((dq, q), (dk, k), (dv, v)):
+        if g.shape != ref.shape or g.stride() != ref.stride() or g.dtype != ref.dtype:
+            raise ValueError("gradient buffers must match the shape, strides and dtype of q/k/v")
+    with torch.cuda.device(q.device):
+        _check(lib.fa_bwd_noalloc(ctypes.byref(p), _ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _stream(q.device)))
     return dq, dk, dv
 
 

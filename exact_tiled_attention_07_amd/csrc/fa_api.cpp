@@ -143,6 +143,36 @@ fa_status check_device() {
   return FA_OK;
 }
 
+// Scratch of fa_bwd_noalloc: the backward's row statistics (two float32
+// arrays of batch * nheads_q * Nq_pad entries, as in a fa_bwd workspace) live
+// in this static device array, so that the call takes no workspace and
+// allocates nothing.  Each GPU holds its own copy until the process ends; its
+// device address is resolved once per device, with that device current, and
+// only that address is handed to kernels (the array's name is a host-side
+// stand-in).  The preprocess stage writes every entry the other two stages
+// read, so nothing in it needs clearing between calls.
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+fa_status device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return FA_OK;
+}
+
 fa::AttnArgs make_args(const fa_params* p) {
   fa::AttnArgs a{};
   a.q_sb = p->q_strides[0]; a.q_sn = p->q_strides[1]; a.q_sh = p->q_strides[2];
@@ -330,9 +360,11 @@ fa_status fa_bwd_workspace_size(const fa_params* params, size_t* bytes) {
 
 namespace {
 
+// noalloc: the row statistics go to this device's static scratch instead of
+// a caller's workspace (fa_bwd_noalloc); workspace arguments are ignored.
 fa_status run_bwd(const fa_params* params, int stages, const void* dout, const void* q, const void* k,
                   const void* v, const void* o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  size_t workspace_bytes, void* stream, bool noalloc = false) {
   fa_status s = check_params(params);
   if (s != FA_OK) return s;
   const bool q_nonempty = !empty_problem(params);
@@ -347,7 +379,13 @@ fa_status run_bwd(const fa_params* params, int stages, const void* dout, const v
   if ((s = check_ptr(dk, "dk", kv_nonempty)) != FA_OK) return s;
   if ((s = check_ptr(dv, "dv", kv_nonempty)) != FA_OK) return s;
   const size_t need = workspace_bytes_for(params);
-  if (need > 0) {
+  if (noalloc) {
+    if (need > kNoallocScratchBytes)
+      return fail(FA_ERR_UNSUPPORTED,
+                  "fa_bwd_noalloc: this problem needs %zu bytes of row statistics, above the %zu bytes of the "
+                  "library's static scratch (call fa_bwd with a workspace instead)",
+                  need, kNoallocScratchBytes);
+  } else if (need > 0) {
     if ((s = check_ptr(workspace, "workspace", true)) != FA_OK) return s;
     if (workspace_bytes < need)
       return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
@@ -361,6 +399,7 @@ fa_status run_bwd(const fa_params* params, int stages, const void* dout, const v
   }
   if (!q_nonempty && !kv_nonempty) return FA_OK;
   if ((s = check_device()) != FA_OK) return s;
+  if (noalloc && (s = device_scratch(&workspace)) != FA_OK) return s;
   fa::AttnArgs a = make_args(params);
   a.q = q; a.k = k; a.v = v; a.o = const_cast<void*>(o); a.lse = const_cast<float*>(lse);
   a.dout = dout; a.dq = dq; a.dk = dk; a.dv = dv;
@@ -381,6 +420,11 @@ fa_status fa_bwd(const fa_params* params, const void* dout, const void* q, const
                  const void* o, const float* lse, void* dq, void* dk, void* dv, void* workspace,
                  size_t workspace_bytes, void* stream) {
   return run_bwd(params, fa::kStageAll, dout, q, k, v, o, lse, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_noalloc(const fa_params* params, const void* dout, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, void* dq, void* dk, void* dv, void* stream) {
+  return run_bwd(params, fa::kStageAll, dout, q, k, v, o, lse, dq, dk, dv, nullptr, 0, stream, true);
 }
 
 fa_status fa_bwd_stage(const fa_params* params, int stage, const void* dout, const void* q, const void* k,

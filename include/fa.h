@@ -178,6 +178,26 @@ fa_status fa_bwd_stage(const fa_params* params, int stage, const void* dout, con
                        void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_bwd without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight training or serving loops, harnesses
+ * that forbid allocation).  Same arguments (minus the workspace), validation,
+ * kernels and results as fa_bwd, bit for bit.  The backward's row statistics
+ * go to a static scratch array inside the library instead: 16 MiB on each GPU
+ * the library runs on, held until the process ends, enough for
+ * batch * nheads_q * Nq_pad <= 2^21 rows (Nq_pad = seqlen_q rounded up to a
+ * multiple of 128; e.g. batch 2 x 32 heads x 32768 queries).  Larger problems
+ * return FA_ERR_UNSUPPORTED before any device work; use fa_bwd for them.
+ * The call allocates nothing (the scratch's device address is looked up once
+ * per device, on the first call made with that device current).  All calls
+ * on one GPU share its scratch and it keeps the last call's contents:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be serialised by the caller.
+ */
+fa_status fa_bwd_noalloc(const fa_params* params, const void* dout, const void* q, const void* k,
+                         const void* v, const void* o, const float* lse, void* dq, void* dk, void* dv,
+                         void* stream);
+
+/*
  * Packed variable-length batches ([P4] section "上手 FlashAttention 的三步走":
  * when the sequences of a batch differ in length, the varlen interfaces take
  * them packed one after another instead of padded).

@@ -3,7 +3,8 @@
 //
 // stdin: one case per line, "<entry> <expected status> <hex bytes of the
 // parameter struct>", where entry is one of
-//   fwd bwd stage0 stage1 stage2 bwd_ws kv kv_ws vl_fwd vl_bwd vl_ws (stageN: fa_bwd_stage N)
+//   fwd bwd stage0 stage1 stage2 bwd_ws bwd_na kv kv_ws vl_fwd vl_bwd vl_ws
+// (stageN: fa_bwd_stage N; bwd_na: fa_bwd_noalloc)
 // Pointer arguments are fixed, distinct, 16-byte aligned fake addresses: the
 // ABI validates them and never dereferences one before its device check.
 // Prints every mismatch; the exit status is the number of mismatches (capped).
@@ -34,7 +35,7 @@ int run(const std::string& entry, const std::vector<unsigned char>& bytes, bool*
   *known = true;
   size_t ws = 0;
   const size_t big = size_t(1) << 30;
-  if (entry == "fwd" || entry == "bwd" || entry == "bwd_ws" || entry.rfind("stage", 0) == 0) {
+  if (entry == "fwd" || entry == "bwd" || entry == "bwd_ws" || entry == "bwd_na" || entry.rfind("stage", 0) == 0) {
     if (bytes.size() != sizeof(fa_params)) return -100;
     fa_params p;
     std::memcpy(&p, bytes.data(), sizeof p);
@@ -43,6 +44,8 @@ int run(const std::string& entry, const std::vector<unsigned char>& bytes, bool*
       return fa_bwd(&p, P(9), P(0), P(1), P(2), P(3), static_cast<float*>(P(4)), P(6), P(7), P(8), P(5), big,
                     nullptr);
     if (entry == "bwd_ws") return fa_bwd_workspace_size(&p, &ws);
+    if (entry == "bwd_na")
+      return fa_bwd_noalloc(&p, P(9), P(0), P(1), P(2), P(3), static_cast<float*>(P(4)), P(6), P(7), P(8), nullptr);
     const int st = entry[5] - '0';
     return fa_bwd_stage(&p, st, P(9), P(0), P(1), P(2), P(3), static_cast<float*>(P(4)), P(6), P(7), P(8), P(5),
                         big, nullptr);

@@ -34,7 +34,7 @@ def header_functions():
 
 def test_header_declares_expected_entry_points():
     assert header_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd_kvcache",
+        ["fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_stage", "fa_bwd_workspace_size", "fa_fwd_kvcache",
          "fa_fwd_kvcache_paged",
          "fa_fwd_kvcache_workspace_size", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_varlen_workspace_size",
          "fa_status_string", "fa_last_error", "fa_version"])
@@ -177,6 +177,32 @@ def test_unsupported_arguments(lib, name, kw):
     assert call_bwd(lib, params(**kw)) == N.FA_ERR_UNSUPPORTED
     for st in STAGES:
         assert call_stage(lib, params(**kw), st) == N.FA_ERR_UNSUPPORTED
+
+
+def call_noalloc(lib, p, dq=0x70000, dk=0x80000, dv=0x90000):
+    pp = ctypes.byref(p) if p is not None else None
+    return lib.fa_bwd_noalloc(pp, 0xA0000, A, B_, C, O, L, dq, dk, dv, None)
+
+
+def test_noalloc_validation(lib):
+    # fa_bwd_noalloc validates exactly as fa_bwd (minus the workspace) and
+    # rejects problems whose row statistics exceed its 16 MiB static scratch,
+    # all before any device call.
+    assert call_noalloc(lib, None) == N.FA_ERR_INVALID_ARG
+    for _, kw in INVALID:
+        assert call_noalloc(lib, params(**kw)) == N.FA_ERR_INVALID_ARG
+    for _, kw in UNSUPPORTED:
+        assert call_noalloc(lib, params(**kw)) == N.FA_ERR_UNSUPPORTED
+    assert call_noalloc(lib, params(), dk=A) == N.FA_ERR_INVALID_ARG  # aliases q
+    # 2^21 rows of statistics fit exactly; one more 128-row block does not.
+    fits = params(batch=1, seqlen_q=32768, seqlen_k=64, nheads_q=64, nheads_kv=2,
+                  q_strides=(32768 * 64 * 64, 64 * 64, 64), o_strides=(32768 * 64 * 64, 64 * 64, 64))
+    big = params(batch=1, seqlen_q=32769, seqlen_k=64, nheads_q=64, nheads_kv=2,
+                 q_strides=(32769 * 64 * 64, 64 * 64, 64), o_strides=(32769 * 64 * 64, 64 * 64, 64))
+    assert call_noalloc(lib, big) == N.FA_ERR_UNSUPPORTED
+    assert b"static scratch" in lib.fa_last_error()
+    assert call_noalloc(lib, fits) == N.FA_ERR_HIP  # valid: reaches the device check (no GPU here)
+    assert call_noalloc(lib, params(batch=0)) == N.FA_OK
 
 
 def test_backward_stage_validation(lib):

@@ -72,14 +72,14 @@ def _matrix():
         lines.append(f"{entry} {int(status)} {bytes(struct).hex()}")
 
     for _, kw in T.INVALID:
-        for e in ("fwd", "bwd", "bwd_ws", "stage0", "stage1", "stage2"):
+        for e in ("fwd", "bwd", "bwd_ws", "stage0", "stage1", "stage2", "bwd_na"):
             add(e, N.FA_ERR_INVALID_ARG, T.params(**kw))
         add("kv", N.FA_ERR_INVALID_ARG, T.kv_params(**kw))
         add("kv_ws", N.FA_ERR_INVALID_ARG, T.kv_params(**kw))
         add("vl_fwd", N.FA_ERR_INVALID_ARG, T.vl_params(**kw))
         add("vl_bwd", N.FA_ERR_INVALID_ARG, T.vl_params(**kw))
     for _, kw in T.UNSUPPORTED:
-        for e in ("fwd", "bwd", "stage0", "stage1", "stage2"):
+        for e in ("fwd", "bwd", "stage0", "stage1", "stage2", "bwd_na"):
             add(e, N.FA_ERR_UNSUPPORTED, T.params(**kw))
     for _, kw in T.KV_UNSUPPORTED:
         add("kv", N.FA_ERR_UNSUPPORTED, T.kv_params(**kw))
@@ -89,8 +89,11 @@ def _matrix():
     add("vl_fwd", N.FA_ERR_UNSUPPORTED, T.vl_params(k_strides=(0, 2 * 64, 68)))
     # Valid calls pass every check and reach the device check or a launcher
     # stub: FA_ERR_HIP either way; the size queries succeed.
-    for e in ("fwd", "bwd", "stage0", "stage1", "stage2"):
+    for e in ("fwd", "bwd", "stage0", "stage1", "stage2", "bwd_na"):
         add(e, N.FA_ERR_HIP, T.params())
+    add("bwd_na", N.FA_ERR_UNSUPPORTED, T.params(batch=1, seqlen_q=32769, seqlen_k=64, nheads_q=64, nheads_kv=2,
+                                                 q_strides=(32769 * 64 * 64, 64 * 64, 64),
+                                                 o_strides=(32769 * 64 * 64, 64 * 64, 64)))
     add("bwd_ws", N.FA_OK, T.params())
     add("kv", N.FA_ERR_HIP, T.kv_params())
     add("kv_ws", N.FA_OK, T.kv_params())
