@@ -338,7 +338,7 @@ struct DkdvWs {
       // the gradient of element [qb][r].
       uint32_t inside[BMQ / 32];
       if constexpr (MOD) {
-        const float slope_r = alibi_raw(a->alibi, a->alibi_sb, a->inv_scale, b, hk * a->G + cu.g);
+        const float slope_r = alibi_raw_uniform(a->alibi, a->alibi_sb, a->inv_scale, b, hk * a->G + cu.g);
         const float base = (float)(i0 + a->delta - key + 4 * hf);  // i' - key of element [0][0]
 #pragma unroll
         for (int qb = 0; qb < BMQ / 32; ++qb) {
@@ -607,8 +607,23 @@ struct DqCtx {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if constexpr (MOD) {
+      // The modifiers in place, before the mask: where the clamp blocks the
+      // gradient, dP is replaced by D, which makes dS = P * (dP - D) exactly
+      // 0; then the score becomes the modified logit.  (A separate pass keeps
+      // the dS loop below as light as the plain kernel's.)
+      const float base = dist0 - (float)j0;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (!(fabsf(s[kb][r]) < cap)) dp[kb][r] = dsum;
+          s[kb][r] = mod_score(s[kb][r], cap, slope_r, base - (float)(32 * kb + 8 * (r >> 2) + (r & 3)));
+        }
+      }
+    }
     const bool full = (j0 >= lo_max) && (j0 + BN - 1 <= hi_min);
-    if (!MOD && !full) {  // with the modifiers the mask follows them, element by element below
+    if (!full) {
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
@@ -628,17 +643,8 @@ struct DqCtx {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * tt + e;
-          float sv = s[kb][r], dv = dp[kb][r];
-          if constexpr (MOD) {
-            // Where the clamp blocks the gradient, dP is replaced by D, which
-            // makes dS = P * (dP - D) exactly 0.
-            if (!(fabsf(sv) < cap)) dv = dsum;
-            sv = mod_score(sv, cap, slope_r, dist0 - (float)(j0 + 32 * kb + 8 * (r >> 2) + (r & 3)));
-            const int kk = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (!full && (kk < lo_i || kk > hi_i)) sv = -INFINITY;
-          }
-          const float pr = fast_exp2(fmaf(sv, c, -lse2));
-          ds[e] = pr * (dv - dsum);
+          const float pr = fast_exp2(fmaf(s[kb][r], c, -lse2));
+          ds[e] = pr * (dp[kb][r] - dsum);
         }
         dsf[2 * kb + tt] = u32x4{T::pack(ds[0], ds[1]), T::pack(ds[2], ds[3]), T::pack(ds[4], ds[5]),
                                  T::pack(ds[6], ds[7])};
@@ -697,7 +703,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
   x.c = a.scale_log2;
   if constexpr (MOD) {
     x.cap = a.cap;
-    x.slope_r = alibi_raw(a.alibi, a.alibi_sb, a.inv_scale, b, hq);
+    x.slope_r = alibi_raw_uniform(a.alibi, a.alibi_sb, a.inv_scale, b, hq);
     x.dist0 = (float)(qrow + a.delta - 4 * hf);
   }
   const uint16_t* Qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh;
@@ -792,7 +798,9 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream, int stages
   const int64_t grid_q = (int64_t)a.B * a.Hkv * n_qt * a.G;
   if (grid_q > 0 && (stages & kStageDq)) {
     if (a.mod)
-      hipLaunchKernelGGL((bwd_dq_kernel<T, D, FA_DQ_BN, FA_DQ_NW, true>), dim3((unsigned)grid_q),
+      // 32-key tiles at d = 128: the modifiers' per-element work does not fit
+      // the registers of 64-key tiles there without spilling.
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, (D == 128 ? 32 : FA_DQ_BN), FA_DQ_NW, true>), dim3((unsigned)grid_q),
                          dim3(FA_DQ_NW * 64), 0, stream, args);
     else
       hipLaunchKernelGGL((bwd_dq_kernel<T, D, FA_DQ_BN, FA_DQ_NW, false>), dim3((unsigned)grid_q),

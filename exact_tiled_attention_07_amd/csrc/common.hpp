@@ -84,6 +84,11 @@ __device__ __forceinline__ float mod_score(float s, float cap, float slope_raw, 
 __device__ __forceinline__ float alibi_raw(const float* alibi, int64_t sb, float inv_scale, int b, int h) {
   return alibi ? alibi[b * sb + h] * inv_scale : 0.f;
 }
+// The same for a (b, h) shared by the whole wave: the slope is then kept in a
+// scalar register instead of one VGPR per lane.
+__device__ __forceinline__ float alibi_raw_uniform(const float* alibi, int64_t sb, float inv_scale, int b, int h) {
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(alibi_raw(alibi, sb, inv_scale, b, h))));
+}
 
 // Binds the arguments to batch entry b of a packed variable-length batch:
 // every pointer moves to the sequence's first row (the workspace rows to

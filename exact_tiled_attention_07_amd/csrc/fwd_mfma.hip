@@ -247,7 +247,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   x.c = a.scale_log2;
   if constexpr (MOD) {
     x.cap = a.cap;
-    x.slope_r = alibi_raw(a.alibi, a.alibi_sb, a.inv_scale, b, hq);
+    x.slope_r = alibi_raw_uniform(a.alibi, a.alibi_sb, a.inv_scale, b, hq);
     x.dist0 = (float)(qrow + a.delta - 4 * hf);
   }
   const uint16_t* Qp = static_cast<const uint16_t*>(a.q) + b * a.q_sb + hq * a.q_sh;

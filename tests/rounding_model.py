@@ -2,9 +2,9 @@
 
 The fp16/bf16 kernels compute in fp32 but round three quantities to the input
 type before a matrix product (the internal-precision reading: products on the
-matrix cores take 16-bit operands): P before O += P V and dV += P^T dO, and
-dS = P (dP - D) before dQ += dS K and dK += dS^T Q; and D_i = sum_c dO_ic O_ic
-is formed from the stored (16-bit) output O.  This module applies exactly those
+matrix cores take 16-bit operands): P before O += P V (forward) and
+dV += P^T dO, and dS = P (dP - D) before dQ += dS K and dK += dS^T Q; and
+D_i = sum_c dO_ic O_ic is formed from the stored (16-bit) forward output O.  This module applies exactly those
 roundings to otherwise exact float64 arithmetic, so that its error against the
 oracle is the error that the rounding policy alone costs.  On inputs whose
 gradients are large or cancel (scores with std 4, keys that climb along the
@@ -34,6 +34,30 @@ def round_to(x, dtype_name):
     return torch.from_numpy(np.ascontiguousarray(x)).to(TORCH_DT[dtype_name]).double().numpy()
 
 
+def _stored_output(s, vis, vh, dtype_name):
+    """The forward's output for one head: unnormalised probabilities (against
+    the row maximum) rounded before the product with V, the fp32 row sum of the
+    unrounded ones, the result rounded at the store."""
+    m = np.max(np.where(vis, s, -np.inf), axis=1, initial=-np.inf)
+    e = np.where(vis, np.exp(s - np.where(np.isfinite(m), m, 0.0)[:, None]), 0.0)
+    tot = e.sum(axis=1)
+    return round_to((round_to(e, dtype_name) @ vh) / np.where(tot > 0, tot, 1.0)[:, None], dtype_name)
+
+
+def policy_fwd(q, k, v, dtype_name, causal=False, window=(-1, -1), scale=None):
+    """O (float64, already rounded to the type) as the forward's rounding policy gives it."""
+    b_, nq, hq, d = q.shape
+    nk, hkv = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = np.zeros_like(q)
+    vis = oracle.visible(nq, nk, causal, window)
+    for b in range(b_):
+        for h in range(hq):
+            g = oracle.head_of(h, hq, hkv)
+            o[b, :, h] = _stored_output(oracle.scores(q[b, :, h], k[b, :, g], scale), vis, v[b, :, g], dtype_name)
+    return o
+
+
 def policy_grads(do, q, k, v, dtype_name, causal=False, window=(-1, -1), scale=None):
     """(dq, dk, dv) in float64 as the kernels' rounding policy gives them
     (before the final rounding of the outputs)."""
@@ -48,8 +72,9 @@ def policy_grads(do, q, k, v, dtype_name, causal=False, window=(-1, -1), scale=N
         for h in range(hq):
             g = oracle.head_of(h, hq, hkv)
             kh, vh, qh, doh = k[b, :, g], v[b, :, g], q[b, :, h], do[b, :, h]
-            p, _ = oracle.masked_softmax(oracle.scores(qh, kh, scale), vis)
-            o_stored = round_to(p @ vh, dtype_name)
+            s = oracle.scores(qh, kh, scale)
+            p, _ = oracle.masked_softmax(s, vis)
+            o_stored = _stored_output(s, vis, vh, dtype_name) if dtype_name else p @ vh
             dp = doh @ vh.T
             dsum = np.sum(doh * o_stored, axis=1)
             ds = round_to(p * (dp - dsum[:, None]), dtype_name)

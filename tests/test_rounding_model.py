@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from exact_tiled_attention_07_amd.workloads import random_qkv
-from rounding_model import policy_grads, round_to
+from rounding_model import policy_fwd, policy_grads, round_to
 
 
 def _f64(*ts):
@@ -37,3 +37,9 @@ def test_model_error_scales_with_the_unit_roundoff(dtype, u):
 def test_round_to_is_round_to_nearest_even():
     x = np.array([1.0 + 2.0 ** -9, 1.0 + 3 * 2.0 ** -9, -2.5])
     assert np.array_equal(round_to(x, "bf16"), [1.0, 1.0 + 2 * 2.0 ** -8, -2.5])
+
+
+def test_forward_model_without_rounding_is_the_oracle():
+    q, k, v, _ = _f64(*random_qkv((1, 45, 4, 16), (1, 45, 1, 16), "fp32", seed=23))
+    o_ref, _ = oracle.attention_fwd(q, k, v, causal=True, window=(7, -1))
+    assert np.allclose(policy_fwd(q, k, v, None, causal=True, window=(7, -1)), o_ref, rtol=1e-12, atol=1e-12)
