@@ -11,7 +11,10 @@ forward (five products per visible score pair instead of two).
 Beside the step, the same line carries a "decode" object: fa_fwd_kvcache
 (in-place append + attention against a ragged KV cache) on the bf16 decode
 workload B=8, one new token, Hq=32, Hkv=8, d=128, capacity 16384, timed per
-call with events and priced against HBM bandwidth (it reads the cache once).
+call with events and priced against HBM bandwidth (it reads the cache once);
+a "next_rows" object (packed variable-length batch, score modifiers); and a
+"configs" object: fa_fwd and fa_bwd timed on their own on every named
+workload at full size (median of 5 runs of --config-calls calls).
 """
 
 import argparse
@@ -85,23 +88,30 @@ def flops(w):
     return fwd, 2.5 * fwd
 
 
-# HBM bytes per launch of the dK/dV kernel on the bench workload, from two
-# rocprofv3 --pmc runs of "python3 bench.py --steps 2 --warmup 1
-# --no-cpu-baseline --decode-calls 5" (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
-# scaled by the factor that the same counter needs to read 512 MiB for the
-# plain copy of "python3 bench.py --copy-probe".  They describe the kernel
-# built from the sources whose SHA-256 is recorded here and are reported as
-# null for any other source.
-DKDV_TRAFFIC = {
-    "sources_sha256": "95ba2e19879ee22bea89f17d14b6938169435cacf99ed1a43f58b3ba405c4795",
-    "bytes_per_launch": 1937298807,
+# Counter-derived figures per launch of the attention kernels on the bench
+# workload, from rocprofv3 --pmc runs of "python3 bench.py --steps 2 --warmup 1
+# --no-cpu-baseline --decode-calls 0 --next-rows-steps 0 --config-calls 0"
+# (profiles/attention_kernels_bf16_b2_hq32_hkv8_n8192_d128_causal_counters.txt):
+#   mfma_busy  SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8), the
+#              share of the cycles the kernel ran at that its matrix cores were busy
+#   traffic    HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
+#              by what the same counter needs to read 512 MiB for the plain copy of
+#              "python3 bench.py --copy-probe"
+# They describe the kernels built from the sources whose SHA-256 is recorded
+# here and are reported as null for any other source.
+COUNTERS = {
+    "sources_sha256": "a1bd97fc17b90bb40358465c3471aa580ae4b2190e0f939ec3e64834d5f28305",
+    "fwd_pp_kernel": {"mfma_busy": 0.615, "traffic": 572700000},
+    "bwd_preprocess_kernel": {"mfma_busy": None, "traffic": 293700000},
+    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.528, "traffic": 1934200000},
+    "bwd_dq_kernel": {"mfma_busy": 0.691, "traffic": 709300000},
 }
 
 
 def kernel_sources_sha():
     import hashlib
     h = hashlib.sha256()
-    for name in ("bwd_mfma.hip", "common.hpp", "tile_io.hpp"):
+    for name in ("fwd_mfma.hip", "bwd_mfma.hip", "common.hpp", "tile_io.hpp"):
         with open(os.path.join(ROOT, "exact_tiled_attention_07_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -126,17 +136,18 @@ def kernel_table(w, f_fwd, f_bwd, ms):
         ("bwd_dq_kernel<BF16,128,64,8> (fa_bwd_stage DQ)", "mfma", 0.2 * f_bwd),
     ]
     out = []
+    sha = kernel_sources_sha()
     for (name, bound, work), t in zip(spec, ms):
         if bound == "mfma":
             ach, peak, unit = work / (t * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
         else:
             ach, peak, unit = work / (t * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
         row = {"kernel": name, "ms": round(t, 4), "bound": bound, "achieved": round(ach, 2), "peak": peak,
-               "unit": unit, "frac": round(ach / peak, 4)}
-        if "dkdv" in name:
-            row["traffic"] = None
-            if DKDV_TRAFFIC and DKDV_TRAFFIC["sources_sha256"] == kernel_sources_sha():
-                row["traffic"] = DKDV_TRAFFIC["bytes_per_launch"]
+               "unit": unit, "frac": round(ach / peak, 4), "mfma_busy": None, "traffic": None}
+        c = COUNTERS.get(name.split("<")[0]) if COUNTERS["sources_sha256"] == sha else None
+        if c:
+            row["mfma_busy"] = c.get("mfma_busy")
+            row["traffic"] = c.get("traffic")
         out.append(row)
     return out
 
@@ -506,6 +517,7 @@ def main():
         "peak": dom["peak"],
         "unit": dom["unit"],
         "frac": dom["frac"],
+        "mfma_busy": dom.get("mfma_busy"),
         "traffic": dom.get("traffic"),
     }
 
