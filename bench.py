@@ -14,7 +14,9 @@ workload B=8, one new token, Hq=32, Hkv=8, d=128, capacity 16384, timed per
 call with events and priced against HBM bandwidth (it reads the cache once);
 a "next_rows" object (packed variable-length batch, score modifiers); and a
 "configs" object: fa_fwd and fa_bwd timed on their own on every named
-workload at full size (median of 5 runs of --config-calls calls).
+workload at full size (median of 5 runs of --config-calls calls); and a
+"memory" object: the peak device memory of one forward + backward beyond the
+inputs, against standard attention that keeps the N x N matrices.
 """
 
 import argparse
@@ -46,6 +48,7 @@ def parse():
                     help="timed steps of the packed-batch and score-modifier legs (0: skip)")
     ap.add_argument("--config-calls", type=int, default=10,
                     help="timed calls per repeat (5 repeats) of each named workload's fwd and bwd (0: skip)")
+    ap.add_argument("--no-memory", action="store_true", help="skip the peak-memory comparison")
     ap.add_argument("--copy-probe", action="store_true",
                     help="instead of the benchmark, run a plain device copy of 512 MiB (read 512 MiB, "
                          "write 512 MiB) 5 times: the known-size reference for HBM byte counters")
@@ -442,6 +445,63 @@ def configs_leg(calls, repeats=5):
     return out
 
 
+def standard_attention_fwd_bwd(q, k, v, do, scale):
+    """Attention the standard way, for the memory comparison only: the full
+    score matrix S, P = softmax(S), O = P V, then the backward from the stored
+    P (dP, dS of the same size).  (batch, heads, seq, d) bf16 tensors; every
+    transposed operand of a batched product is made contiguous first."""
+    import torch
+    s_ = torch.matmul(q, k.transpose(-2, -1).contiguous()) * scale
+    n = s_.shape[-1]
+    mask = torch.ones(n, n, dtype=torch.bool, device=q.device).triu(1)
+    s_.masked_fill_(mask, float("-inf"))
+    p = torch.softmax(s_, dim=-1)
+    del s_
+    o = torch.matmul(p, v)
+    dv = torch.matmul(p.transpose(-2, -1).contiguous(), do)
+    dp = torch.matmul(do, v.transpose(-2, -1).contiguous())
+    dsum = (do * o).sum(-1, keepdim=True)
+    ds = p * (dp - dsum)
+    del dp
+    dq = torch.matmul(ds, k) * scale
+    dk = torch.matmul(ds.transpose(-2, -1).contiguous(), q) * scale
+    return o, dq, dk, dv
+
+
+def memory_leg():
+    """Peak device memory of one forward + backward beyond the inputs (q, k, v,
+    dO), this library against standard attention that keeps the N x N matrices,
+    at the pages' memory-benchmark shape: bf16, hidden 2048 = 16 heads x d 128,
+    batch 1, causal, N = 2048 and 4096."""
+    import torch
+
+    import exact_tiled_attention_07_amd as fa
+    from exact_tiled_attention_07_amd.workloads import random_qkv
+
+    out = {"shape": "bf16, batch 1, 16 heads x d 128, causal", "unit": "MiB beyond the inputs"}
+    for n in (2048, 4096):
+        q, k, v, do = (t.cuda() for t in random_qkv((1, n, 16, 128), (1, n, 16, 128), "bf16", seed=77))
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        o, lse = fa.fwd(q, k, v, causal=True)
+        g = fa.bwd(do, q, k, v, o, lse, causal=True)
+        torch.cuda.synchronize()
+        ours = torch.cuda.max_memory_allocated() - base
+        del o, lse, g
+        qh, kh, vh, doh = (t.transpose(1, 2).contiguous() for t in (q, k, v, do))
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        r = standard_attention_fwd_bwd(qh, kh, vh, doh, 1.0 / 128 ** 0.5)
+        torch.cuda.synchronize()
+        std = torch.cuda.max_memory_allocated() - base
+        del r, qh, kh, vh, doh
+        out[f"N{n}"] = {"this_library": round(ours / 2 ** 20, 1), "standard": round(std / 2 ** 20, 1),
+                        "ratio": round(std / ours, 1)}
+    return out
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -554,6 +614,8 @@ def main():
         out["next_rows"] = next_rows_leg(args.next_rows_steps)
     if args.config_calls > 0:
         out["configs"] = configs_leg(args.config_calls)
+    if not args.no_memory:
+        out["memory"] = memory_leg()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q_c, k_c, v_c, do_c, args.cpu_seconds)
     print(json.dumps(out), flush=True)
