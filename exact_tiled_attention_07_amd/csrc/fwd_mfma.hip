@@ -36,6 +36,10 @@ namespace fa {
 // maximum keeps being the reference, so probabilities stay below 2^kLazyRescale.
 // O and l always share the same reference, so the result is unchanged.
 static constexpr float kLazyRescale = 8.0f;
+// A lane's share of a tile's row sum below this bound proves that none of its
+// probabilities exceeds 2^kLazyRescale (2^8 less 1/1024 of it, well beyond the
+// rounding of the exponent and of exp2).
+static constexpr float kLazyBound = 256.0f - 0.25f;
 
 // Launch configuration (tuned on MI355X; overridable at build time).
 #ifndef FA_FWD_BN
@@ -173,26 +177,41 @@ struct FwdPP {
     }
     // The reference maximum moves only when some row of the wave grew by more
     // than 2^kLazyRescale; then O and l (which hold the tiles up to m - 1) are
-    // rescaled.
-    // Row maximum: four independent chains, then the lane pair.
-    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // rescaled.  P is first computed against the current reference: if every
+    // lane's share of the tile's row sum stays below kLazyBound, no probability
+    // exceeds 2^kLazyRescale, so no row maximum grew that far and the reference
+    // and P stand.  Otherwise (or while some row has no reference yet) the row
+    // maximum decides exactly as it would have up front, and P is recomputed
+    // if the reference moved.  The bound sits a little below 2^kLazyRescale so
+    // that the rounding of the two tests can never let a rescale slip through.
+    float ls = exp_pack(mref);
+    if (__any(!(ls <= kLazyBound) || mref == -INFINITY)) {
+      // Row maximum: four independent chains, then the lane pair.
+      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
+      for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
+        for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
+      }
+      const float mx = max_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+      if (__any((mx - mref) * c > kLazyRescale)) {  // false for NaN (both -inf)
+        const float m_new = fmaxf(mref, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((mref - m_new) * c);
+        mref = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        ls = exp_pack(mref);
+      }
     }
-    const float mx = max_xor32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-    if (__any((mx - mref) * c > kLazyRescale)) {  // false for NaN (both -inf)
-      const float m_new = fmaxf(mref, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((mref - m_new) * c);
-      mref = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-    }
-    const float mc = (mref == -INFINITY) ? 0.f : mref * c;
-    // Row sum of this tile in four partial sums (short dependency chains).
-    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+    l += ls;
+  }
+
+  // P^T = exp2(s*c - ref*c) rounded into pf; returns this lane's share of the
+  // tile's row sum (of the unrounded probabilities), in four partial sums.
+  __device__ __forceinline__ float exp_pack(float ref) {
+    const float mc = (ref == -INFINITY) ? 0.f : ref * c;
+    float l4[4];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
@@ -201,12 +220,15 @@ struct FwdPP {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           p[e] = fast_exp2(fmaf(s[kb][8 * tt + e], c, -mc));
-          l4[e & 3] += p[e];
+          if (kb == 0 && tt == 0 && e < 4)
+            l4[e] = p[e];
+          else
+            l4[e & 3] += p[e];
         }
         pf[2 * kb + tt] = u32x4{T::pack(p[0], p[1]), T::pack(p[2], p[3]), T::pack(p[4], p[5]), T::pack(p[6], p[7])};
       }
     }
-    l += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+    return (l4[0] + l4[1]) + (l4[2] + l4[3]);
   }
 };
 
@@ -268,8 +290,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   x.hi_i = key_hi(a, qrow);
   const int q_last = min(q0 + BM, a.Nq) - 1;
   const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
-  x.lo_max = key_lo(a, q_last);
-  x.hi_min = key_hi(a, q0);
+  // Tiles that every query of this wave sees in full skip the element mask.
+  const int wq0 = q0 + 32 * __builtin_amdgcn_readfirstlane(wave);
+  x.lo_max = key_lo(a, min(wq0 + 31, a.Nq - 1));
+  x.hi_min = key_hi(a, wq0);
   x.t_lo = kv_lo / BN;
   x.n = (kv_hi >= kv_lo) ? kv_hi / BN - x.t_lo + 1 : 0;
 
