@@ -140,6 +140,7 @@ struct DmaTile {
   static constexpr int PER_WAVE = (NBLK + NW - 1) / NW;
   static_assert(ROWS % RPB == 0, "tile rows must fill whole 1 KB blocks");
   uint32_t off[PER_WAVE];  // byte offsets of this lane's chunk in each of its blocks
+  uint32_t tail;           // bytes of a row that hold data (16 * dch)
 
   // dch = 16-byte chunks of a row that hold data (head dim / 8, <= D / 8).  A
   // lane whose chunk lies past it loads chunk 0 of the same row instead (valid
@@ -155,13 +156,17 @@ struct DmaTile {
       const int c = lane_pc ^ Swz<D>::sw(r);
       off[i] = (uint32_t)(r * row_stride_elems * 2 + (c < dch ? c : 0) * 16);
     }
+    tail = (uint32_t)dch * 16u;
   }
   // Rows row0 .. row0+ROWS-1 of a tensor whose rows start every row_stride
-  // elements; rows at or beyond nrows read as zeros.
+  // elements; rows at or beyond nrows read as zeros.  The resource ends with
+  // the data of the last row, so a single row is read whole whatever its
+  // stride (a tensor of one row may carry any stride, 0 included).
   __device__ __forceinline__ void issue(const uint16_t* base, int64_t row_stride, int row0, int nrows,
                                         uint16_t* lds_tile, int wave) const {
     const int rows = min(max(nrows - row0, 0), ROWS);
-    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(base + (int64_t)row0 * row_stride, (uint32_t)(rows * row_stride * 2));
+    const uint32_t bytes = rows > 0 ? (uint32_t)((rows - 1) * row_stride * 2) + tail : 0u;
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(base + (int64_t)row0 * row_stride, bytes);
     const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {

@@ -232,6 +232,32 @@ def test_strided_packed_qkv_matches_contiguous():
         assert torch.equal(a.contiguous(), b)
 
 
+@pytest.mark.parametrize("which", ["kv", "q"])
+def test_single_row_any_stride(which):
+    # A tensor of one row along the sequence may carry any stride there, 0
+    # included (an expanded view): the results equal those of contiguous copies.
+    _note(f"single row, sequence stride 0: {which}")
+    nq, nk = (70, 1) if which == "kv" else (1, 90)
+    q, _, _, do = random_qkv((2, nq, 4, 128), (2, nq, 2, 128), "bf16", seed=31)
+    _, k, v, _ = random_qkv((2, nk, 4, 128), (2, nk, 2, 128), "bf16", seed=32)
+    q, k, v, do = (t.cuda() for t in (q, k, v, do))
+
+    def zero_row_stride(t):
+        return t.as_strided(t.shape, (t.stride(0), 0, t.stride(2), t.stride(3)))
+
+    qs, ks, vs = (zero_row_stride(q), k, v) if which == "q" else (q, zero_row_stride(k), zero_row_stride(v))
+    for mask in (dict(), dict(causal=True)):
+        o1, l1 = fa.fwd(qs, ks, vs, **mask)
+        o2, l2 = fa.fwd(q, k, v, **mask)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), mask
+        g1 = fa.bwd(do, qs, ks, vs, o2, l2, **mask)
+        g2 = fa.bwd(do, q, k, v, o2, l2, **mask)
+        torch.cuda.synchronize()
+        for a, b in zip(g1, g2):
+            assert torch.equal(a.contiguous(), b.contiguous()), mask
+
+
 def test_autograd_wrapper_matches_bwd():
     q, k, v, do = (t.cuda() for t in random_qkv((1, 150, 4, 64), (1, 150, 2, 64), "fp16", seed=16))
     qr, kr, vr = (t.clone().requires_grad_() for t in (q, k, v))
