@@ -16,7 +16,9 @@ a "next_rows" object (packed variable-length batch, score modifiers); and a
 "configs" object: fa_fwd and fa_bwd timed on their own on every named
 workload at full size (median of 5 runs of --config-calls calls); and a
 "memory" object: the peak device memory of one forward + backward beyond the
-inputs, against standard attention that keeps the N x N matrices.
+inputs, against standard attention that keeps the N x N matrices; and a
+"gemm_reference" object: the vendor library's bf16 GEMM rate on the same chip,
+the dense matrix-core throughput it sustains under load.
 """
 
 import argparse
@@ -49,6 +51,7 @@ def parse():
     ap.add_argument("--config-calls", type=int, default=10,
                     help="timed calls per repeat (5 repeats) of each named workload's fwd and bwd (0: skip)")
     ap.add_argument("--no-memory", action="store_true", help="skip the peak-memory comparison")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the vendor bf16 GEMM reference rate")
     ap.add_argument("--copy-probe", action="store_true",
                     help="instead of the benchmark, run a plain device copy of 512 MiB (read 512 MiB, "
                          "write 512 MiB) 5 times: the known-size reference for HBM byte counters")
@@ -502,6 +505,31 @@ def memory_leg():
     return out
 
 
+def gemm_leg(n=8192, reps=20):
+    """Context for the MFMA roofline: the vendor library's bf16 GEMM (torch.matmul,
+    which dispatches to hipBLASLt) on n x n x n, timed with events after warm-up.
+    It is the dense matrix-core rate the chip sustains under load (clock and power
+    included), next to the nameplate peak the roofline uses."""
+    import torch
+
+    g = torch.Generator(device="cuda").manual_seed(3)
+    a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda", generator=g)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda", generator=g)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tflops = 2.0 * n ** 3 / ms / 1e9
+    return {"what": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt)", "ms": round(ms, 4), "tflops": round(tflops, 1),
+            "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -616,6 +644,8 @@ def main():
         out["configs"] = configs_leg(args.config_calls)
     if not args.no_memory:
         out["memory"] = memory_leg()
+    if not args.no_gemm:
+        out["gemm_reference"] = gemm_leg()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q_c, k_c, v_c, do_c, args.cpu_seconds)
     print(json.dumps(out), flush=True)
