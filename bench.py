@@ -106,13 +106,12 @@ def flops(w):
 # They describe the kernels built from the sources whose SHA-256 is recorded
 # here and are reported as null for any other source.
 COUNTERS = {
-    "sources_sha256": "a1bd97fc17b90bb40358465c3471aa580ae4b2190e0f939ec3e64834d5f28305",
-    "fwd_pp_kernel": {"mfma_busy": 0.615, "traffic": 572700000},
+    "sources_sha256": "b2f2b570013a02492b38042cccedfd1a9e8b5c36b1c027c8fe4acdeb02a801c9",
+    "fwd_pp_kernel": {"mfma_busy": 0.613, "traffic": 572700000},
     "bwd_preprocess_kernel": {"mfma_busy": None, "traffic": 293700000},
-    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.528, "traffic": 1934200000},
-    "bwd_dq_kernel": {"mfma_busy": 0.691, "traffic": 709300000},
+    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.524, "traffic": 1931100000},
+    "bwd_dq_kernel": {"mfma_busy": 0.693, "traffic": 708900000},
 }
-
 
 def kernel_sources_sha():
     import hashlib
