@@ -1,6 +1,10 @@
-"""Randomised parity: seeded draws of dtype, head dim, GQA group, lengths,
-mask, scale and memory layout, each run through fa_fwd and fa_bwd and
-compared with the float64 oracle by the same rule as the other parity tests.
+"""Randomised parity over memory layouts and the 16-bit rounding bound.
+
+It complements test_random_gpu.py (which draws the score modifiers and paged
+caches): seeded draws of dtype, head dim, GQA group, lengths, mask, scale and
+memory layout (contiguous, rows padded past the head dim, heads sliced out of
+a wider tensor), each run through fa_fwd and fa_bwd, packed batches through
+the varlen entry points, and KV-cache calls, all against the float64 oracle.
 
 Case i draws from its own seed (10000 + i), so a failure names a case that
 reruns alone (pytest -k "case_17").  Lengths stay small (at most 260) so the
