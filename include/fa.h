@@ -119,8 +119,10 @@ typedef struct {
  *   lse [out] float32 (batch, nheads_q, seqlen_q), dense
  *   stream  hipStream_t or NULL
  * Requirements: all pointers 16-byte aligned and every stride a multiple of
- * 16 bytes (else FA_ERR_UNSUPPORTED).  Results are bitwise repeatable for
- * identical inputs and launch configuration.
+ * 16 bytes; sequence strides at most 2^22 elements and, when the sequence has
+ * more than one row, at least headdim (else FA_ERR_UNSUPPORTED).  A sequence
+ * of one row may carry any stride, 0 included.  Results are bitwise
+ * repeatable for identical inputs and launch configuration.
  */
 fa_status fa_fwd(const fa_params* params, const void* q, const void* k, const void* v,
                  void* o, float* lse, void* stream);
