@@ -14,7 +14,8 @@ workload B=8, one new token, Hq=32, Hkv=8, d=128, capacity 16384, timed per
 call with events and priced against HBM bandwidth (it reads the cache once);
 a "next_rows" object (packed variable-length batch, score modifiers); and a
 "configs" object: fa_fwd and fa_bwd timed on their own on every named
-workload at full size (median of 5 runs of --config-calls calls); and a
+workload at full size (median of 5 runs of at least --config-calls calls and
+about 2 ms of work each); and a
 "memory" object: the peak device memory of one forward + backward beyond the
 inputs, against standard attention that keeps the N x N matrices; and a
 "gemm_reference" object: the vendor library's bf16 GEMM rate on the same chip,
@@ -49,7 +50,8 @@ def parse():
     ap.add_argument("--next-rows-steps", type=int, default=10,
                     help="timed steps of the packed-batch and score-modifier legs (0: skip)")
     ap.add_argument("--config-calls", type=int, default=10,
-                    help="timed calls per repeat (5 repeats) of each named workload's fwd and bwd (0: skip)")
+                    help="minimum timed calls per repeat (5 repeats of at least 2 ms) of each named workload's "
+                         "fwd and bwd (0: skip)")
     ap.add_argument("--no-memory", action="store_true", help="skip the peak-memory comparison")
     ap.add_argument("--no-gemm", action="store_true", help="skip the vendor bf16 GEMM reference rate")
     ap.add_argument("--copy-probe", action="store_true",
@@ -377,13 +379,14 @@ def next_rows_leg(steps):
     return out
 
 
-def configs_leg(calls, repeats=5):
+def configs_leg(calls, repeats=5, min_ms=2.0, max_calls=2000):
     """fa_fwd alone and fa_bwd alone (on the forward's outputs) on every named
     workload at its full size, inputs resident in HBM, outputs preallocated,
-    no cache flush between calls: 3 warm-up calls, then `repeats` runs of
-    `calls` calls between two events on the launch stream; the median run's
-    average per call.  fp16/bf16 rates are set against the dense MFMA peak;
-    the fp32 path runs on the vector ALU and is not rated."""
+    no cache flush between calls: warm-up calls, then `repeats` runs of
+    max(`calls`, about `min_ms` of work) calls between two events on the
+    launch stream; the median run's average per call.  fp16/bf16 rates are
+    set against the dense MFMA peak; the fp32 path runs on the vector ALU and
+    is not rated."""
     import statistics
 
     import torch
@@ -393,8 +396,8 @@ def configs_leg(calls, repeats=5):
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    out = {"calls_per_repeat": calls, "repeats": repeats, "statistic": "median of repeats",
-           "cache": "not flushed between calls"}
+    out = {"min_calls_per_repeat": calls, "min_ms_per_repeat": min_ms, "repeats": repeats,
+           "statistic": "median of repeats", "cache": "not flushed between calls"}
     for name, w in WORKLOADS.items():
         q, k, v, do = (t.to(dev) for t in make_inputs(w))
         kw = dict(causal=w.causal, window_size=w.window)
@@ -410,32 +413,44 @@ def configs_leg(calls, repeats=5):
             fa.bwd(do, q, k, v, o, lse, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
 
         def time_it(fn):
+            # 3 warm-up calls, then 10 timed ones that size the repeats: each
+            # repeat holds at least `calls` calls and at least min_ms of work, so
+            # that the latency of the first launch does not dominate small
+            # workloads.
             for _ in range(3):
                 fn()
             torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            est = e0.elapsed_time(e1) / 10
+            n = max(calls, min(max_calls, math.ceil(min_ms / max(est, 1e-3))))
             runs = []
             for _ in range(repeats):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                for _ in range(calls):
+                for _ in range(n):
                     fn()
                 e1.record(stream)
                 torch.cuda.synchronize()
-                runs.append(e0.elapsed_time(e1) / calls)
-            return statistics.median(runs)
+                runs.append(e0.elapsed_time(e1) / n)
+            return statistics.median(runs), n
 
         f_fwd, f_bwd = flops(w)
         rated = w.dtype != "fp32"
         entry = {"dtype": w.dtype, "shape": [w.batch, w.seqlen, w.nheads_q, w.nheads_kv, w.headdim],
                  "causal": w.causal, "window": list(w.window), "sigma": w.sigma}
-        fm = time_it(fwd)
-        entry.update(fwd_ms=round(fm, 4), fwd_tflops=round(f_fwd / (fm * 1e-3) / 1e12, 2))
+        fm, n = time_it(fwd)
+        entry.update(fwd_ms=round(fm, 4), fwd_tflops=round(f_fwd / (fm * 1e-3) / 1e12, 2), fwd_calls=n)
         if rated:
             entry["fwd_frac"] = round(f_fwd / (fm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
         if w.backward:
             fwd()
-            bm = time_it(bwd)
-            entry.update(bwd_ms=round(bm, 4), bwd_tflops=round(f_bwd / (bm * 1e-3) / 1e12, 2))
+            bm, n = time_it(bwd)
+            entry.update(bwd_ms=round(bm, 4), bwd_tflops=round(f_bwd / (bm * 1e-3) / 1e12, 2), bwd_calls=n)
             tf = (f_fwd + f_bwd) / ((fm + bm) * 1e-3) / 1e12
             entry["fwd_bwd_tflops"] = round(tf, 2)
             if rated:

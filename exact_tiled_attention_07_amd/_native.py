@@ -189,6 +189,32 @@ def make_params(q, k, v, o, *, causal=False, window_size=(-1, -1), scale=None, a
     return p
 
 
+# make_params results of recent dense calls, keyed on everything make_params
+# reads, with the backward workspace size once it has been asked for.  A call
+# with ALiBi slopes carries a device pointer in its parameters and is not kept.
+_PARAMS_CACHE = {}
+_PARAMS_CACHE_MAX = 256
+
+
+def _dense_params(q, k, v, o, causal, window_size, scale, alibi_slopes, softcap):
+    """[FaParams, workspace bytes or None] for fwd/bwd; the FaParams is shared
+    between calls and must not be modified."""
+    if alibi_slopes is not None:
+        return [make_params(q, k, v, o, causal=causal, window_size=window_size, scale=scale,
+                            alibi_slopes=alibi_slopes, softcap=softcap), None]
+    key = (q.shape, q.stride(), k.shape, k.stride(), v.shape, v.stride(), o.shape, o.stride(), q.dtype, k.dtype,
+           v.dtype, o.dtype, bool(causal), tuple(window_size), None if scale is None else float(scale),
+           float(softcap))
+    entry = _PARAMS_CACHE.get(key)
+    if entry is None:
+        entry = [make_params(q, k, v, o, causal=causal, window_size=window_size, scale=scale, softcap=softcap),
+                 None]
+        if len(_PARAMS_CACHE) >= _PARAMS_CACHE_MAX:
+            _PARAMS_CACHE.clear()
+        _PARAMS_CACHE[key] = entry
+    return entry
+
+
 def _require_gpu(*ts):
     for t in ts:
         if not t.is_cuda:
@@ -217,8 +243,7 @@ def fwd(q, k, v, *, causal=False, window_size=(-1, -1), scale=None, out=None, ls
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
-    p = make_params(q, k, v, out, causal=causal, window_size=window_size, scale=scale, alibi_slopes=alibi_slopes,
-                    softcap=softcap)
+    p = _dense_params(q, k, v, out, causal, window_size, scale, alibi_slopes, softcap)[0]
     with torch.cuda.device(q.device):
         _check(lib.fa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q.device)))
     return out, lse
@@ -249,15 +274,17 @@ def bwd(dout, q, k, v, out, lse, *, causal=False, window_size=(-1, -1), scale=No
     if lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[0], q.shape[2], q.shape[1]) \
             or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (batch, nheads_q, seqlen_q) tensor")
-    p = make_params(q, k, v, out, causal=causal, window_size=window_size, scale=scale, alibi_slopes=alibi_slopes,
-                    softcap=softcap)
+    entry = _dense_params(q, k, v, out, causal, window_size, scale, alibi_slopes, softcap)
+    p = entry[0]
     dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if dq is None else dq
     dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device) if dk is None else dk
     dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device) if dv is None else dv
     for g, ref in ((dq, q), (dk, k), (dv, v)):
         if g.shape != ref.shape or g.stride() != ref.stride() or g.dtype != ref.dtype:
             raise ValueError("gradient buffers must match the shape, strides and dtype of q/k/v")
-    need = bwd_workspace_size(p)
+    if entry[1] is None:
+        entry[1] = bwd_workspace_size(p)
+    need = entry[1]
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ptrs = (_ptr(dout), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),

@@ -292,6 +292,52 @@ def test_python_binding_rejects_cpu_tensors():
         fa.fwd(q, q, q)
 
 
+def _struct_bytes(p):
+    return bytes(memoryview(p).cast("B"))
+
+
+def test_memoised_params_match_fresh_params():
+    """fwd/bwd reuse the FaParams of an earlier call with the same shapes,
+    strides, dtypes and options; the reused struct must be byte-identical to
+    a fresh make_params, and any change in those inputs must build a new one."""
+    import torch
+    N._PARAMS_CACHE.clear()
+    q = torch.zeros(2, 8, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(2, 16, 2, 64, dtype=torch.bfloat16)
+    base = dict(causal=True, window_size=(-1, -1), scale=None, softcap=0.0)
+    variants = [
+        (q, k, k, q, base),
+        (q, k, k, q, dict(base, causal=False)),
+        (q, k, k, q, dict(base, window_size=(3, 0))),
+        (q, k, k, q, dict(base, window_size=[3, 0])),
+        (q, k, k, q, dict(base, scale=0.5)),
+        (q, k, k, q, dict(base, softcap=30.0)),
+        (q.transpose(1, 2).contiguous().transpose(1, 2), k, k, q, base),
+        (q, k[:, :8], k[:, :8], q, base),
+        (q.half(), k.half(), k.half(), q.half(), base),
+    ]
+    seen = {}
+    for qq, kk, vv, oo, kw in variants:
+        first = N._dense_params(qq, kk, vv, oo, kw["causal"], kw["window_size"], kw["scale"], None, kw["softcap"])
+        again = N._dense_params(qq, kk, vv, oo, kw["causal"], kw["window_size"], kw["scale"], None, kw["softcap"])
+        assert again is first
+        fresh = N.make_params(qq, kk, vv, oo, **kw)
+        assert _struct_bytes(first[0]) == _struct_bytes(fresh)
+        seen.setdefault(_struct_bytes(fresh), set()).add(id(first[0]))
+    # one cached struct per distinct parameter set (the list and tuple windows share one)
+    assert len(seen) == len(variants) - 1
+    assert all(len(ids) == 1 for ids in seen.values())
+    # a call with ALiBi slopes carries a pointer and is never served from the cache
+    slopes = torch.zeros(4, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        N._dense_params(q, k, k, q, True, (-1, -1), None, slopes, 0.0)
+    # invalid layouts are still rejected, cached or not
+    with pytest.raises(ValueError, match="headdim"):
+        strided_d = torch.zeros(2, 8, 64, 4, dtype=torch.bfloat16).transpose(2, 3)
+        N._dense_params(strided_d, k, k, q, True, (-1, -1), None, None, 0.0)
+    N._PARAMS_CACHE.clear()
+
+
 def test_missing_library_fails_loudly(tmp_path):
     code = ("import exact_tiled_attention_07_amd._native as N; N.LIB_PATH = '/nonexistent/libfa.so'\n"
             "try:\n    N.load_library()\nexcept RuntimeError as e:\n    print('RAISED', 'missing' in str(e))\n")
