@@ -214,10 +214,10 @@ struct DkdvWs {
     const int i0 = row_of(cu), hq = hk * a->G + cu.g;
     if (Q)
       qd.issue(static_cast<const uint16_t*>(a->q) + b * a->q_sb + hq * a->q_sh, a->q_sn, i0, a->Nq,
-               reinterpret_cast<uint16_t*>(slot_tiles(slot)), kb);
+               reinterpret_cast<uint16_t*>(slot_tiles(slot)));
     if (DO)
       dd.issue(static_cast<const uint16_t*>(a->dout) + b * a->o_sb + hq * a->o_sh, a->o_sn, i0, a->Nq,
-               reinterpret_cast<uint16_t*>(slot_tiles(slot) + L::TILE * 2), kb);
+               reinterpret_cast<uint16_t*>(slot_tiles(slot) + L::TILE * 2));
     if (Q && kb == L::KW - 1) {
       const int64_t ro = b * a->ws_sb + hq * a->ws_sh + i0;
       uint16_t* r = reinterpret_cast<uint16_t*>(slot_stats(slot));
@@ -578,8 +578,8 @@ struct DqCtx {
     const int j0 = t * BN;
     if (t < t_hi) {
       if (wave >= NW - NLW) {
-        kd.issue(Kp, k_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE, wave - (NW - NLW));
-        vd.issue(Vp, v_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE + TILE, wave - (NW - NLW));
+        kd.issue(Kp, k_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE);
+        vd.issue(Vp, v_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE + TILE);
       }
     }
     // S^T = K Q^T and dP^T = V dO^T; element [kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
@@ -742,8 +742,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
 
   if (t_lo <= x.t_hi) {
     if (wave >= NW - Ctx::NLW) {
-      x.kd.issue(x.Kp, a.k_sn, t_lo * BN, a.Nk, smem, wave - (NW - Ctx::NLW));
-      x.vd.issue(x.Vp, a.v_sn, t_lo * BN, a.Nk, smem + Ctx::TILE, wave - (NW - Ctx::NLW));
+      x.kd.issue(x.Kp, a.k_sn, t_lo * BN, a.Nk, smem);
+      x.vd.issue(x.Vp, a.v_sn, t_lo * BN, a.Nk, smem + Ctx::TILE);
     }
     wait_all_loads();
   }

@@ -88,6 +88,7 @@ struct FwdPP {
   float cap, slope_r, dist0;  // score modifiers (MOD): clamp, raw slope, i' - 4*hf of this lane
   f32x16 oacc[D / 32];
   f32x16 s[BN / 32];  // scores of tile m between its MFMA and softmax intervals
+  u32x4 ring[FA_FWD_RING];  // LDS operands in flight (the first NB - 1 read before the interval's barrier)
   u32x4 pf[BN / 16];  // P^T of tile m between its softmax and the next MFMA interval
 
   static constexpr int NPV = (BN / 16) * (D / 32), NS = (D / 16) * (BN / 32);
@@ -120,9 +121,6 @@ struct FwdPP {
     static_assert(NPV >= NB, "interval shape");
     const char* Vs = reinterpret_cast<const char*>(vbuf + (1 - PAR) * TILE);
     const char* Ks = reinterpret_cast<const char*>(kbuf + PAR * TILE);
-    u32x4 ring[NB];
-#pragma unroll
-    for (int o = 0; o < NB - 1; ++o) ring[o % NB] = operand(Vs, Ks, o);
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
 #pragma unroll
@@ -144,10 +142,23 @@ struct FwdPP {
     // loads V(m+1) into the V buffer whose last reader is this very interval
     // (B's product with V(m-1); A's was in interval 2m).
     if (group_a) {
-      if (m + 1 < n) kd.issue(Kp, k_sn, (t_lo + m + 1) * BN, Nk, kbuf + (1 - PAR) * TILE, wave);
+      if (m + 1 < n) kd.issue_nonempty(Kp, k_sn, (t_lo + m + 1) * BN, Nk, kbuf + (1 - PAR) * TILE);
     } else {
-      if (m + 1 < n) vd.issue(Vp, v_sn, (t_lo + m + 1) * BN, Nk, vbuf + (1 - PAR) * TILE, wave - HALF);
+      if (m + 1 < n) vd.issue_nonempty(Vp, v_sn, (t_lo + m + 1) * BN, Nk, vbuf + (1 - PAR) * TILE);
     }
+  }
+
+  // The first NB - 1 operands of the next MFMA interval (buffer parity PAR),
+  // read before the barrier that opens it, so that its first MFMA does not
+  // wait out an LDS round trip after the barrier.  They come from the V tile
+  // of that interval's P V product, which an earlier barrier published.
+  template <int PAR>
+  __device__ __forceinline__ void prefetch() {
+    constexpr int NB = FA_FWD_RING;
+    const char* Vs = reinterpret_cast<const char*>(vbuf + (1 - PAR) * TILE);
+    const char* Ks = reinterpret_cast<const char*>(kbuf + PAR * TILE);
+#pragma unroll
+    for (int o = 0; o < NB - 1; ++o) ring[o % NB] = operand(Vs, Ks, o);
   }
 
   // Softmax interval of tile m: mask, row max, lazy rescale of O and l, P.
@@ -328,9 +339,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   x.vd.init(wave % Ctx::HALF, lane, a.v_sn, a.D / 8);
   if (x.n > 0) {
     if (group_a)
-      x.kd.issue(x.Kp, a.k_sn, x.t_lo * BN, a.Nk, kbuf, wave);
+      x.kd.issue(x.Kp, a.k_sn, x.t_lo * BN, a.Nk, kbuf);
     else
-      x.vd.issue(x.Vp, a.v_sn, x.t_lo * BN, a.Nk, vbuf, wave - Ctx::HALF);
+      x.vd.issue(x.Vp, a.v_sn, x.t_lo * BN, a.Nk, vbuf);
     wait_all_loads();
   }
   __syncthreads();
@@ -339,16 +350,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int n = x.n;
   int m = 0;
   if (group_a) {
+    x.template prefetch<0>();
     for (; m + 1 <= n; m += 2) {
       x.template mfma_interval<0>(m, true);
       lds_barrier();
       x.softmax_interval(m);
       wait_all_loads();
+      x.template prefetch<1>();
       lds_barrier();
       x.template mfma_interval<1>(m + 1, true);
       lds_barrier();
       x.softmax_interval(m + 1);
       wait_all_loads();
+      x.template prefetch<0>();
       lds_barrier();
     }
     if (m <= n) {
@@ -362,11 +376,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (; m + 1 <= n; m += 2) {
       x.softmax_interval(m - 1);
       wait_all_loads();
+      x.template prefetch<0>();
       lds_barrier();
       x.template mfma_interval<0>(m, false);
       lds_barrier();
       x.softmax_interval(m);
       wait_all_loads();
+      x.template prefetch<1>();
       lds_barrier();
       x.template mfma_interval<1>(m + 1, false);
       lds_barrier();
@@ -374,6 +390,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (m <= n) {
       x.softmax_interval(m - 1);
       wait_all_loads();
+      x.template prefetch<0>();
       lds_barrier();
       x.template mfma_interval<0>(m, false);
       lds_barrier();

@@ -140,13 +140,18 @@ struct DmaTile {
   static constexpr int PER_WAVE = (NBLK + NW - 1) / NW;
   static_assert(ROWS % RPB == 0, "tile rows must fill whole 1 KB blocks");
   uint32_t off[PER_WAVE];  // byte offsets of this lane's chunk in each of its blocks
-  uint32_t tail;           // bytes of a row that hold data (16 * dch)
+  uint32_t tail;           // bytes of a row that hold data (16 * dch); wave-uniform
+  int wv;                  // this wave's index among the NW loading waves; wave-uniform
 
   // dch = 16-byte chunks of a row that hold data (head dim / 8, <= D / 8).  A
   // lane whose chunk lies past it loads chunk 0 of the same row instead (valid
   // memory, no per-load test): the kernels pair those LDS columns only with
   // zero register columns or with outputs that are never stored.  Row strides
-  // are at most 2^22 elements, so every offset fits 32 bits.
+  // are at most 2^22 elements, so every offset fits 32 bits.  The wave-uniform
+  // values are read from the first lane here, so that issue() runs on the
+  // scalar unit alone: a vector instruction in it would wait behind the other
+  // wave of the SIMD, which is streaming its softmax through the vector unit
+  // while this wave finishes its matrix products.
   __device__ __forceinline__ void init(int wave, int lane, int64_t row_stride_elems, int dch = D / 8) {
     const int lane_row = lane / CPR, lane_pc = lane % CPR;
 #pragma unroll
@@ -156,18 +161,30 @@ struct DmaTile {
       const int c = lane_pc ^ Swz<D>::sw(r);
       off[i] = (uint32_t)(r * row_stride_elems * 2 + (c < dch ? c : 0) * 16);
     }
-    tail = (uint32_t)dch * 16u;
+    tail = __builtin_amdgcn_readfirstlane((uint32_t)dch * 16u);
+    wv = __builtin_amdgcn_readfirstlane(wave);
   }
   // Rows row0 .. row0+ROWS-1 of a tensor whose rows start every row_stride
   // elements; rows at or beyond nrows read as zeros.  The resource ends with
   // the data of the last row, so a single row is read whole whatever its
-  // stride (a tensor of one row may carry any stride, 0 included).
+  // stride (a tensor of one row may carry any stride, 0 included).  base,
+  // row_stride, row0, nrows and lds_tile must be wave-uniform.
   __device__ __forceinline__ void issue(const uint16_t* base, int64_t row_stride, int row0, int nrows,
-                                        uint16_t* lds_tile, int wave) const {
+                                        uint16_t* lds_tile) const {
     const int rows = min(max(nrows - row0, 0), ROWS);
     const uint32_t bytes = rows > 0 ? (uint32_t)((rows - 1) * row_stride * 2) + tail : 0u;
-    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(base + (int64_t)row0 * row_stride, bytes);
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    dma(raw_rsrc(base + (int64_t)row0 * row_stride, bytes), lds_tile);
+  }
+  // The same for a tile that holds at least one row (row0 < nrows).  Without
+  // the clamp at zero rows the arithmetic stays on the scalar unit; the
+  // clamped form above is combined into a vector med3.
+  __device__ __forceinline__ void issue_nonempty(const uint16_t* base, int64_t row_stride, int row0, int nrows,
+                                                 uint16_t* lds_tile) const {
+    const int rows = min(nrows - row0, ROWS);
+    const uint32_t bytes = (uint32_t)((rows - 1) * row_stride * 2) + tail;
+    dma(raw_rsrc(base + (int64_t)row0 * row_stride, bytes), lds_tile);
+  }
+  __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t rs, uint16_t* lds_tile) const {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int j = wv + i * NW;
