@@ -578,8 +578,8 @@ struct DqCtx {
     const int j0 = t * BN;
     if (t < t_hi) {
       if (wave >= NW - NLW) {
-        kd.issue(Kp, k_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE);
-        vd.issue(Vp, v_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE + TILE);
+        kd.issue_nonempty(Kp, k_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE);
+        vd.issue_nonempty(Vp, v_sn, j0 + BN, Nk, smem + (1 - BUF) * 2 * TILE + TILE);
       }
     }
     // S^T = K Q^T and dP^T = V dO^T; element [kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
@@ -633,7 +633,14 @@ struct DqCtx {
         }
       }
     }
-    // dS^T = P^T * (dP^T - D) as B operands, then dQ^T += K^T dS^T.
+    // dS^T = P^T * (dP^T - D) as B operands, then dQ^T += K^T dS^T; the first
+    // transposed K operands of the dQ product are read before the dS loop, so
+    // that they have arrived when its MFMAs start.
+    constexpr int QNB = FA_DQ_RING, QNO = (BN / 16) * (D / 32);
+    u32x4 qring[QNB];
+#pragma unroll
+    for (int o = 0; o < QNB - 1; ++o) qring[o] = off.tr_operand(Ks, o / (D / 32), o % (D / 32));
+    __builtin_amdgcn_sched_barrier(0);
     u32x4 dsf[BN / 16];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
@@ -651,18 +658,14 @@ struct DqCtx {
       }
     }
     {
-      constexpr int NB = FA_DQ_RING, NO = (BN / 16) * (D / 32);
-      u32x4 ring[NB];
 #pragma unroll
-      for (int o = 0; o < NB - 1; ++o) ring[o] = off.tr_operand(Ks, o / (D / 32), o % (D / 32));
-#pragma unroll
-      for (int o = 0; o < NO; ++o) {
-        if (o + NB - 1 < NO) {
-          const int nx = o + NB - 1;
-          ring[nx % NB] = off.tr_operand(Ks, nx / (D / 32), nx % (D / 32));
+      for (int o = 0; o < QNO; ++o) {
+        if (o + QNB - 1 < QNO) {
+          const int nx = o + QNB - 1;
+          qring[nx % QNB] = off.tr_operand(Ks, nx / (D / 32), nx % (D / 32));
         }
         __builtin_amdgcn_sched_barrier(0);
-        dqa[o % (D / 32)] = T::mfma(ring[o % NB], dsf[o / (D / 32)], dqa[o % (D / 32)]);
+        dqa[o % (D / 32)] = T::mfma(qring[o % QNB], dsf[o / (D / 32)], dqa[o % (D / 32)]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -195,8 +195,17 @@ struct FwdPP {
     // maximum decides exactly as it would have up front, and P is recomputed
     // if the reference moved.  The bound sits a little below 2^kLazyRescale so
     // that the rounding of the two tests can never let a rescale slip through.
-    float ls = exp_pack(mref);
-    if (__any(!(ls <= kLazyBound) || mref == -INFINITY)) {
+    // With score modifiers (a steep ALiBi slope moves the maximum on every
+    // tile, and the clamp and distance make the vector work the longer half
+    // of the interval) the row maximum is always taken first, so that P is
+    // computed once.  Both orders take the same decisions.
+    float ls = 0.f;
+    bool check = true;
+    if constexpr (!MOD) {
+      ls = exp_pack(mref);
+      check = __any(!(ls <= kLazyBound) || mref == -INFINITY);
+    }
+    if (check) {
       // Row maximum: four independent chains, then the lane pair.
       float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -212,9 +221,10 @@ struct FwdPP {
         l *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-        ls = exp_pack(mref);
+        if constexpr (!MOD) ls = exp_pack(mref);
       }
     }
+    if constexpr (MOD) ls = exp_pack(mref);
     l += ls;
   }
 
