@@ -108,12 +108,13 @@ def flops(w):
 # They describe the kernels built from the sources whose SHA-256 is recorded
 # here and are reported as null for any other source.
 COUNTERS = {
-    "sources_sha256": "b2f2b570013a02492b38042cccedfd1a9e8b5c36b1c027c8fe4acdeb02a801c9",
-    "fwd_pp_kernel": {"mfma_busy": 0.613, "traffic": 572700000},
+    "sources_sha256": "dcfd08278f515d5041bfd94ff29304029e7da9e331efdb72018b3b4a46e736f8",
+    "fwd_pp_kernel": {"mfma_busy": 0.655, "traffic": 572900000},
     "bwd_preprocess_kernel": {"mfma_busy": None, "traffic": 293700000},
-    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.524, "traffic": 1931100000},
-    "bwd_dq_kernel": {"mfma_busy": 0.693, "traffic": 708900000},
+    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.524, "traffic": 1921800000},
+    "bwd_dq_kernel": {"mfma_busy": 0.685, "traffic": 709500000},
 }
+
 
 def kernel_sources_sha():
     import hashlib
