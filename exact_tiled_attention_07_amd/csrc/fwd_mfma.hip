@@ -177,12 +177,19 @@ struct FwdPP {
     }
     const bool full = (j0 >= lo_max) && (j0 + BN - 1 <= hi_min);
     if (!full) {
+      // Element key j = kbase + k_r (k_r a constant of the register) is
+      // visible iff (j - lo) | (hi - j) has its sign bit clear; the sign bit,
+      // spread over the word, selects -inf (bit pattern 0xff800000) with one
+      // bitfield insert.  No lane masks are held in scalar registers.
+      const int kbase = j0 + 4 * hf;
+      const int a0 = kbase - lo_i, b0 = hi_i - kbase;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key < lo_i || key > hi_i) s[kb][r] = -INFINITY;
+          const int kr = 32 * kb + 8 * (r >> 2) + (r & 3);
+          const uint32_t out = (uint32_t)(((a0 + kr) | (b0 - kr)) >> 31);
+          s[kb][r] = __uint_as_float((out & 0xff800000u) | (~out & __float_as_uint(s[kb][r])));
         }
       }
     }
