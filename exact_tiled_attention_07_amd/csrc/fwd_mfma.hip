@@ -181,7 +181,12 @@ struct FwdPP {
       // visible iff (j - lo) | (hi - j) has its sign bit clear; the sign bit,
       // spread over the word, selects -inf (bit pattern 0xff800000) with one
       // bitfield insert.  No lane masks are held in scalar registers.
-      const int kbase = j0 + 4 * hf;
+      // (j0 passes through an empty asm so that the compiler does not turn
+      // a0 and b0 into per-lane induction variables stepped on every tile,
+      // which would put vector adds into the MFMA interval's load block.)
+      int jj = j0;
+      asm volatile("" : "+s"(jj));
+      const int kbase = jj + 4 * hf;
       const int a0 = kbase - lo_i, b0 = hi_i - kbase;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
