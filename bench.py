@@ -108,11 +108,11 @@ def flops(w):
 # They describe the kernels built from the sources whose SHA-256 is recorded
 # here and are reported as null for any other source.
 COUNTERS = {
-    "sources_sha256": "dcfd08278f515d5041bfd94ff29304029e7da9e331efdb72018b3b4a46e736f8",
-    "fwd_pp_kernel": {"mfma_busy": 0.655, "traffic": 572900000},
+    "sources_sha256": "7d3807e7606ba9478bfcffb067451da0ef11d2d9e72e2ab446f8d3b7c14e6c64",
+    "fwd_pp_kernel": {"mfma_busy": 0.677, "traffic": 574300000},
     "bwd_preprocess_kernel": {"mfma_busy": None, "traffic": 293700000},
-    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.524, "traffic": 1921800000},
-    "bwd_dq_kernel": {"mfma_busy": 0.685, "traffic": 709500000},
+    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.525, "traffic": 1928200000},
+    "bwd_dq_kernel": {"mfma_busy": 0.695, "traffic": 709200000},
 }
 
 
