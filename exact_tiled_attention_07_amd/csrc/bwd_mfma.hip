@@ -334,33 +334,12 @@ struct DkdvWs {
     lds_barrier();  // the gradient waves have taken the previous item's P and dS
     if (w < n_items) {
       const int i0 = row_of(cu);
-      // Score modifiers; bit r of inside[qb] records whether the clamp passes
-      // the gradient of element [qb][r].
-      uint32_t inside[BMQ / 32];
-      if constexpr (MOD) {
-        const float slope_r = alibi_raw_uniform(a->alibi, a->alibi_sb, a->inv_scale, b, hk * a->G + cu.g);
-        const float base = (float)(i0 + a->delta - key + 4 * hf);  // i' - key of element [0][0]
-#pragma unroll
-        for (int qb = 0; qb < BMQ / 32; ++qb) {
-          inside[qb] = 0u;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            inside[qb] |= (fabsf(s[qb][r]) < a->cap ? 1u : 0u) << r;
-            s[qb][r] = mod_score(s[qb][r], a->cap, slope_r, base + (float)(32 * qb + 8 * (r >> 2) + (r & 3)));
-          }
-        }
-      }
       const int i_end = min(i0 + BMQ, a->Nq) - 1;
       const bool full = (key_lo(*a, i_end) <= k0) && (key_hi(*a, i0) >= k_last);
-      if (!full) {
-#pragma unroll
-        for (int qb = 0; qb < BMQ / 32; ++qb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = i0 + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (int(key < key_lo(*a, i)) | int(key > key_hi(*a, i))) s[qb][r] = -INFINITY;
-          }
-        }
+      float slope_r = 0.f, base = 0.f;
+      if constexpr (MOD) {
+        slope_r = alibi_raw_uniform(a->alibi, a->alibi_sb, a->inv_scale, b, hk * a->G + cu.g);
+        base = (float)(i0 + a->delta - key + 4 * hf);  // i' - key of element [0][0]
       }
       const float* lse2s = reinterpret_cast<const float*>(slot_stats(slot));
       const float* dsums = lse2s + BMQ;
@@ -374,6 +353,23 @@ struct DkdvWs {
           l4[g4] = *reinterpret_cast<const f32x4*>(lse2s + 32 * qb + 8 * g4 + 4 * hf);
           d4[g4] = *reinterpret_cast<const f32x4*>(dsums + 32 * qb + 8 * g4 + 4 * hf);
         }
+        if constexpr (MOD) {
+          // Score modifiers, before the mask.  Where the clamp blocks the
+          // gradient, dP is replaced by D, which makes dS = P * (dP - D)
+          // exactly 0 without keeping a gate per element.
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if (!(fabsf(s[qb][r]) < a->cap)) dp[qb][r] = d4[r >> 2][r & 3];
+            s[qb][r] = mod_score(s[qb][r], a->cap, slope_r, base + (float)(32 * qb + 8 * (r >> 2) + (r & 3)));
+          }
+        }
+        if (!full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = i0 + 32 * qb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (int(key < key_lo(*a, i)) | int(key > key_hi(*a, i))) s[qb][r] = -INFINITY;
+          }
+        }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           float pb[8], db_[8];
@@ -383,7 +379,6 @@ struct DkdvWs {
             const float pr = fast_exp2(fmaf(s[qb][r], c, -l4[r >> 2][r & 3]));
             pb[e] = pr;
             db_[e] = pr * (dp[qb][r] - d4[r >> 2][r & 3]);
-            if constexpr (MOD) db_[e] = ((inside[qb] >> r) & 1u) ? db_[e] : 0.f;
           }
           const int si = 2 * qb + tt;
           *reinterpret_cast<u32x4*>(pimg + si * 1024) =
