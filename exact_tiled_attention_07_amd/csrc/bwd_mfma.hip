@@ -459,63 +459,6 @@ struct DkdvWs {
   }
 };
 
-// Packed causal batches without a left window: the key tiles of one kv head
-// differ in work with their sequence's lengths -- tile t of a sequence of Lq
-// queries and Lk keys is seen by Lq - max(0, BNK*t - (Lk - Lq)) queries -- so
-// slot s of an XCD (workgroup ids go round-robin over the 8 XCDs) takes the
-// s-th heaviest (unit, tile) pair among the units that XCD holds, longest
-// first, which balances the end of the grid.  Ties go by unit, then tile.  The
-// pair is found by bisection on the work, one unit per lane (at most 64 units
-// per XCD); every wave of the workgroup finds the same pair.  Returns false
-// for a slot past the last pair.
-template <int BNK>
-__device__ bool lpt_causal_tile(const AttnArgs& a, int w, int n_units, int& unit, int& tile) {
-  const int xcd = w & 7, s = w >> 3, per = n_units >> 3;
-  const int lane = threadIdx.x & 63;
-  int lq = 0, lk = 0, nt = 0;
-  if (lane < per) {
-    const int b = (lane * 8 + xcd) / a.Hkv;  // the lengths of bind_seq
-    const int q0 = min(max(a.cu_q[b], 0), a.total_q), q1 = min(max(a.cu_q[b + 1], q0), a.total_q);
-    const int k0 = min(max(a.cu_k[b], 0), a.total_k), k1 = min(max(a.cu_k[b + 1], k0), a.total_k);
-    lq = min(q1 - q0, a.Nq);
-    lk = min(k1 - k0, a.Nk);
-    nt = (lk + BNK - 1) / BNK;
-  }
-  const int delta = lk - lq;
-  // Pairs of this lane's unit seen by at least W queries (W >= 0; every tile
-  // of a unit counts for W = 0, also one that no query sees: its dK and dV
-  // are still written, as zeros).
-  auto count = [&](int W) {
-    const int e = lq - W + delta;
-    return (lane < per && W <= lq && e >= 0) ? min(nt, e / BNK + 1) : 0;
-  };
-  constexpr unsigned long long kAll = ~0ull;
-  if (__reduce_add_sync(kAll, count(0)) <= s) return false;
-  int lo = 0, hi = a.Nq + 1;  // count(lo) > s >= count(hi), summed over the units
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (__reduce_add_sync(kAll, count(mid)) > s)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  // The s-th pair has work lo; idx is its rank among the pairs of that work.
-  int idx = s - __reduce_add_sync(kAll, count(lo + 1));
-  const int neq = count(lo) - count(lo + 1);
-  for (int u = 0; u < per; ++u) {
-    const int n = __builtin_amdgcn_readlane(neq, u);
-    if (idx < n) {
-      const int lq_u = __builtin_amdgcn_readlane(lq, u), delta_u = __builtin_amdgcn_readlane(delta, u);
-      unit = u * 8 + xcd;
-      // Work lq is taken by tiles 0 .. delta/BNK; any other work by one tile.
-      tile = (lo == lq_u) ? idx : (lq_u - lo + delta_u) / BNK;
-      return true;
-    }
-    idx -= n;
-  }
-  return false;
-}
-
 template <class T, int D, int BMQ, bool MOD>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_ws_kernel(AttnArgs a) {
@@ -532,7 +475,7 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
   WorkItem it;
   if (a.cu_q && a.causal && a.wl < 0 && a.xcd_remap && a.B * a.Hkv <= 8 * 64) {
     int unit = 0, tile = 0;
-    if (!lpt_causal_tile<L::BNK>(a, blockIdx.x, a.B * a.Hkv, unit, tile)) return;
+    if (!lpt_causal_key_tile<L::BNK>(a, blockIdx.x, a.B * a.Hkv, unit, tile)) return;
     it.unit = unit;
     it.tile = tile;
     it.sub = 0;

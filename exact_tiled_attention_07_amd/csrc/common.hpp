@@ -290,4 +290,68 @@ __device__ __forceinline__ WorkItem decode_work(int w, int n_units, int n_tiles,
   return it;
 }
 
+// ---------------------------------------------------------------------------
+// Longest first for the key tiles of packed causal batches (no left window),
+// in the dK/dV kernel.  Tile t (TILE keys) of a sequence of lq queries and lk
+// keys is seen by max(0, lq - max(0, TILE*t - delta)) queries, delta = lk - lq,
+// so the key tiles of a packed batch differ in work with their sequence's
+// lengths, and the grid, sized by the longest sequence, holds many slots past
+// a short sequence's end.  Slot s of an XCD (workgroup ids go round-robin over
+// the 8 XCDs) therefore takes the s-th heaviest (unit, tile) pair of the units
+// that XCD holds -- ties by unit, then tile, ascending -- and slots past the
+// last pair leave at once, after all the work.  A tile that no query sees
+// still runs (it writes zeros).  The pair is found by bisection on the work,
+// one unit per lane (at most 64 units per XCD); every wave of a workgroup
+// finds the same pair.  Returns false for a slot past the last pair.  (The
+// forward and dQ kernels keep the tile-index order of decode_work: their
+// tiles' work grows with the tile index alone, and the same bisection there
+// ran the packed forward 2.7% slower.)
+// ---------------------------------------------------------------------------
+template <int TILE>
+__device__ __forceinline__ bool lpt_causal_key_tile(const AttnArgs& a, int w, int n_units, int& unit, int& tile) {
+  const int xcd = w & 7, s = w >> 3, per = n_units >> 3;
+  const int lane = threadIdx.x & 63;
+  int lq = 0, lk = 0, nt = 0;
+  if (lane < per) {
+    const int b = (lane * 8 + xcd) / a.Hkv;  // the lengths bind_seq gives the sequence
+    const int q0 = min(max(a.cu_q[b], 0), a.total_q), q1 = min(max(a.cu_q[b + 1], q0), a.total_q);
+    const int k0 = min(max(a.cu_k[b], 0), a.total_k), k1 = min(max(a.cu_k[b + 1], k0), a.total_k);
+    lq = min(q1 - q0, a.Nq);
+    lk = min(k1 - k0, a.Nk);
+    nt = (lk + TILE - 1) / TILE;
+  }
+  const int delta = lk - lq;
+  // Tiles of this lane's unit seen by at least W queries (W >= 0).
+  auto count = [&](int W) -> int {
+    const int e = lq - W + delta;
+    return (lane < per && W <= lq && e >= 0) ? min(nt, e / TILE + 1) : 0;
+  };
+  constexpr unsigned long long kAll = ~0ull;
+  if (__reduce_add_sync(kAll, count(0)) <= s) return false;
+  int lo = 0, hi = a.Nq + 1;  // pairs of work >= lo exceed s; of work >= hi do not
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (__reduce_add_sync(kAll, count(mid)) > s)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  // The s-th pair has work lo; idx is its rank among the pairs of that work.
+  int idx = s - __reduce_add_sync(kAll, count(lo + 1));
+  const int neq = count(lo) - count(lo + 1);
+  for (int u = 0; u < per; ++u) {
+    const int n = __builtin_amdgcn_readlane(neq, u);
+    if (idx < n) {
+      const int lq_u = __builtin_amdgcn_readlane(lq, u), d_u = __builtin_amdgcn_readlane(delta, u);
+      unit = u * 8 + xcd;
+      // Work lq (or 0 for a unit without queries) is taken by the tiles from 0
+      // up to delta / TILE; any other work by exactly one tile.
+      tile = (lo == lq_u) ? idx : (lq_u - lo + d_u) / TILE;
+      return true;
+    }
+    idx -= n;
+  }
+  return false;
+}
+
 }  // namespace fa
