@@ -108,13 +108,12 @@ def flops(w):
 # They describe the kernels built from the sources whose SHA-256 is recorded
 # here and are reported as null for any other source.
 COUNTERS = {
-    "sources_sha256": "7d3807e7606ba9478bfcffb067451da0ef11d2d9e72e2ab446f8d3b7c14e6c64",
-    "fwd_pp_kernel": {"mfma_busy": 0.677, "traffic": 574300000},
+    "sources_sha256": "afb71dcd7a1f3d973d8b8972eab8b3da477dd807a366ae94983b23496cf4e696",
+    "fwd_pp_kernel": {"mfma_busy": 0.673, "traffic": 572900000},
     "bwd_preprocess_kernel": {"mfma_busy": None, "traffic": 293700000},
-    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.525, "traffic": 1928200000},
-    "bwd_dq_kernel": {"mfma_busy": 0.695, "traffic": 709200000},
+    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.514, "traffic": 1943100000},
+    "bwd_dq_kernel": {"mfma_busy": 0.688, "traffic": 709300000},
 }
-
 
 def kernel_sources_sha():
     import hashlib

@@ -103,6 +103,45 @@ def test_varlen_sweep(dtype, d, mask):
             assert bool((t == SENTINEL).all()), f"{name} written outside every sequence"
 
 
+# Packed causal batches whose (sequence, kv head) count is a multiple of 8 and
+# at most 512: the dK/dV kernel hands each workgroup the next-heaviest key tile
+# of its XCD's share (longest first), so every key tile of every sequence,
+# empty ones included, must still be visited exactly once.
+LPT_CASES = [
+    # (lens_q, lens_k, hq, hkv)
+    ([300, 0, 17, 129, 1, 64, 0, 200], [300, 12, 0, 129, 257, 64, 40, 17], 32, 8),
+    ([513, 1, 64, 1000], [513, 1, 64, 1000], 16, 8),
+    ([5, 1] * 32, [70, 1] * 32, 8, 8),                 # 64 sequences x 8 kv heads: 512 units
+    ([0, 90, 33, 0], [129, 90, 0, 0], 8, 2),           # Hkv 2, 4 sequences: 8 units
+]
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
+def test_varlen_causal_longest_first_key_tiles(dtype, d):
+    for ci, (lq, lk, hq, hkv) in enumerate(LPT_CASES):
+        assert (len(lq) * hkv) % 8 == 0 and len(lq) * hkv <= 512
+        _note(f"varlen longest-first {dtype} d={d} hq={hq} hkv={hkv} lens_q={lq} lens_k={lk}")
+        q, k, v, do, cu_q, cu_k = _draw(lq, lk, hq, hkv, d, dtype, seed=900 + ci, extra=2)
+        o, lse, dq, dk, dv = _run(q, k, v, do, cu_q, cu_k, max(lq), max(lk), causal=True)
+        o_ref, lse_ref = oracle.attention_fwd_varlen(f64(q), f64(k), f64(v), cu_q.numpy(), cu_k.numpy(),
+                                                     causal=True)
+        g_ref = oracle.attention_bwd_varlen(f64(do), f64(q), f64(k), f64(v), cu_q.numpy(), cu_k.numpy(),
+                                            causal=True)
+        tq, tk = sum(lq), sum(lk)
+        tol = TOL[q.dtype]
+        assert_close(o[:tq], o_ref[:tq], tol, "O")
+        assert_close(lse[:, :tq], lse_ref[:, :tq], tol, "LSE")
+        assert_close(dq[:tq], g_ref[0][:tq], 2 * tol, "dq")
+        assert_close(dk[:tk], g_ref[1][:tk], 2 * tol, "dk")
+        assert_close(dv[:tk], g_ref[2][:tk], 2 * tol, "dv")
+        for b in range(len(lq)):
+            k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+            if lq[b] == 0 and k1 > k0:  # keys that no query sees get zero gradients
+                assert bool((dk[k0:k1] == 0).all()) and bool((dv[k0:k1] == 0).all()), b
+        for name, t in (("o", o[tq:]), ("dq", dq[tq:]), ("dk", dk[tk:]), ("dv", dv[tk:])):
+            assert bool((t == SENTINEL).all()), f"{name} written outside every sequence"
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_varlen_sequences_equal_fixed_length_calls_bitwise(dtype):
     lq = [130, 1, 64, 257, 33]
