@@ -469,7 +469,8 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int n_kt = (a.Nk + L::BNK - 1) / L::BNK;
+  const int tpg = work_tiles_per_group(a, 1);
+  const int n_kt = padded_tiles((a.Nk + L::BNK - 1) / L::BNK, tpg);
   // Under a causal mask the first key tiles see the most queries: run them
   // first (for a packed batch, the heaviest tiles of all its sequences first).
   WorkItem it;
@@ -480,7 +481,7 @@ void bwd_dkdv_ws_kernel(AttnArgs a) {
     it.tile = tile;
     it.sub = 0;
   } else {
-    it = decode_work(blockIdx.x, a.B * a.Hkv, n_kt, 1, false, a.xcd_remap);
+    it = decode_work(blockIdx.x, a.B * a.Hkv, n_kt, 1, false, a.xcd_remap, tpg);
   }
 
   DkdvWs<T, D, BMQ, MOD> x;
@@ -689,9 +690,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int n_qt = (a.Nq + BM - 1) / BM;
+  const int tpg = work_tiles_per_group(a, a.G);
+  const int n_qt = padded_tiles((a.Nq + BM - 1) / BM, tpg);
   const bool heavy_last = (a.causal || a.wr >= 0) && a.wl < 0;
-  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_qt, a.G, heavy_last, a.xcd_remap);
+  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_qt, a.G, heavy_last, a.xcd_remap, tpg);
   const int b = it.unit / a.Hkv, hk = it.unit % a.Hkv;
   const int hq = hk * a.G + it.sub;
   const int q0 = it.tile * BM;
@@ -790,7 +792,7 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream, int stages
   AttnArgs args = a;
   args.xcd_remap = a.xcd_remap && ((a.B * a.Hkv) % 8 == 0);
   using WL = DkdvWsLayout<D, FA_DKDV_BMQ>;
-  const int n_kt = (a.Nk + WL::BNK - 1) / WL::BNK;
+  const int n_kt = padded_tiles((a.Nk + WL::BNK - 1) / WL::BNK, work_tiles_per_group(a, 1));
   const int64_t grid_kv = (int64_t)a.B * a.Hkv * n_kt;
   if (grid_kv > 0 && (stages & kStageDkdv)) {
     if (a.mod)
@@ -802,7 +804,7 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream, int stages
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int n_qt = (a.Nq + FA_DQ_NW * 32 - 1) / (FA_DQ_NW * 32);
+  const int n_qt = padded_tiles((a.Nq + FA_DQ_NW * 32 - 1) / (FA_DQ_NW * 32), work_tiles_per_group(a, a.G));
   const int64_t grid_q = (int64_t)a.B * a.Hkv * n_qt * a.G;
   if (grid_q > 0 && (stages & kStageDq)) {
     if (a.mod)

@@ -266,27 +266,52 @@ struct WorkItem {
   int sub;    // index inside the unit's group (query head offset)
 };
 
+// Inside an XCD, consecutive slots behave as if handed to its four shader
+// engines in turn, each workgroup waiting for a free CU of its own engine: a
+// packed batch whose long sequence's workgroups took every other pair of
+// slots (the rest empty) ran 35% slower than with groups of four slots of
+// equal work.  With
+// fixed lengths the units at one tile index do equal work, so the tile-major
+// order keeps the engines even.  In a packed batch the units differ in
+// length, and slots past a short sequence's end are empty.  With n_sub = 2
+// (mod 4) items per (unit, tile), the items of tpg = 2 consecutive tiles of
+// one unit take consecutive slots, so that every group of four slots holds
+// nearly equal work, and the order of the two tiles alternates from group to
+// group, so that over two groups every engine gets the same tiles' worth
+// (in the forward with head pairs, a packed batch of the benchmark's heads
+// took 9% less time, and a batch of one long and one short sequence 26% less,
+// than in the tile-major order).  With
+// an odd n_sub the same grouping over four tiles ran a packed MHA forward no
+// faster than the tile-major order, which is kept there (work_tiles_per_group).
+// n_tiles is padded to a multiple of tpg (padded_tiles); the padding tiles lie
+// past every sequence's end.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int work_tiles_per_group(const AttnArgs& a, int n_sub) {
+  return (a.cu_q && n_sub % 4 == 2) ? 2 : 1;
+}
+// tpg is 1 or 2.
+__host__ __device__ __forceinline__ int padded_tiles(int n_tiles, int tpg) { return (n_tiles + tpg - 1) & -tpg; }
+
 __device__ __forceinline__ WorkItem decode_work(int w, int n_units, int n_tiles, int n_sub,
-                                                bool heavy_last_first, bool xcd_remap) {
+                                                bool heavy_last_first, bool xcd_remap, int tpg = 1) {
   WorkItem it;
-  int slot, ui, per;
+  int t, per, xcd = 0;
   if (xcd_remap) {
-    const int xcd = w & 7;
-    slot = w >> 3;
+    xcd = w & 7;
+    const int slot = w >> 3;
     per = n_units >> 3;  // units per XCD (host guarantees n_units % 8 == 0)
     it.sub = slot % n_sub;
-    const int t = slot / n_sub;
-    ui = t % per;
-    const int tr = t / per;
-    it.unit = ui * 8 + xcd;
-    it.tile = heavy_last_first ? (n_tiles - 1 - tr) : tr;
+    t = slot / n_sub;
   } else {
+    per = n_units;
     it.sub = w % n_sub;
-    const int t = w / n_sub;
-    it.unit = t % n_units;
-    const int tr = t / n_units;
-    it.tile = heavy_last_first ? (n_tiles - 1 - tr) : tr;
+    t = w / n_sub;
   }
+  const int t1 = t & (tpg - 1), r = t >> (tpg >> 1);  // tpg is 1 or 2
+  const int g = r / per;  // tile group
+  const int tr = g * tpg + ((g & 1) ? (tpg - 1 - t1) : t1);
+  it.unit = xcd_remap ? (r % per) * 8 + xcd : r % per;
+  it.tile = heavy_last_first ? (n_tiles - 1 - tr) : tr;
   return it;
 }
 

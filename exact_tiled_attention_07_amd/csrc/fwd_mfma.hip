@@ -7,8 +7,9 @@
 // that the full score matrix never exists.  The output is the exact attention
 // result; the kernel also writes the per-row log-sum-exp for the backward pass.
 //
-// gfx950 mapping.  One workgroup = 8 waves = a tile of 256 queries of one
-// (batch, query head); each wave owns 32 query rows.  For every K/V tile of
+// gfx950 mapping.  One workgroup = 8 waves = 256 query rows: a tile of 256
+// queries of one (batch, query head), or of 128 queries of two query heads
+// that share a K/V head; each wave owns 32 query rows.  For every K/V tile of
 // BN keys:
 //   S^T (BN x 32) = K Q^T      A operand = K rows from LDS, B = Q (registers)
 //   online softmax             lane l holds query l%32 and 16 keys per 32x32
@@ -48,6 +49,19 @@ static constexpr float kLazyBound = 256.0f - 0.25f;
 #ifndef FA_FWD_RING
 #define FA_FWD_RING 3  // LDS operands in flight ahead of the MFMA that uses them
 #endif
+
+// Query heads per workgroup.  The 256 query rows of a workgroup are either
+// 256 rows of one query head or, when the GQA group size is even, the same 128
+// rows of two query heads that read the same K/V head (wave group A one head,
+// group B the other).  Under a causal mask a workgroup's key range then ends
+// where its last query row's does for both groups, instead of two 64-key
+// tiles later than group A needs (forward 1.4-1.9% faster at N = 8192, 13%
+// at N = 512, batch 8).  A packed batch pairs heads only when the group size is a
+// multiple of 4, so that each (unit, tile) keeps an even number of workgroups
+// (decode_work: with one per (unit, tile) a packed batch of G = 2 ran 5% slower).
+__host__ __device__ __forceinline__ int fwd_heads_per_workgroup(const AttnArgs& a) {
+  return (a.G % (a.cu_q ? 4 : 2) == 0) ? 2 : 1;
+}
 
 // ---------------------------------------------------------------------------
 // Forward with two wave groups in ping-pong.
@@ -278,13 +292,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int l32 = lane & 31, hf = lane >> 5;
   const bool group_a = wave < Ctx::HALF;
 
-  const int n_qt = (a.Nq + BM - 1) / BM;
+  // With an even GQA group the two wave groups take the same 128 query rows
+  // of two query heads that share the K/V head (fwd_heads_per_workgroup).
+  const int hp = fwd_heads_per_workgroup(a);
+  const int lg_rows = (hp == 2) ? 7 : 8;                 // query rows per head: BM / hp
+  static_assert(BM == 256, "rows per head are 256 or 128");
+  const int wr = (hp == 2) ? (wave & (Ctx::HALF - 1)) : wave;  // row block of this wave
+  const int n_sub = a.G >> (hp - 1);
+  const int tpg = work_tiles_per_group(a, n_sub);
+  const int n_qt = padded_tiles((a.Nq + (1 << lg_rows) - 1) >> lg_rows, tpg);
   const bool heavy_last = (a.causal || a.wr >= 0) && a.wl < 0;
-  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_qt, a.G, heavy_last, a.xcd_remap);
+  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_qt, n_sub, heavy_last, a.xcd_remap, tpg);
   const int b = it.unit / a.Hkv, hk = it.unit % a.Hkv;
-  const int hq = hk * a.G + it.sub;
-  const int q0 = it.tile * BM;
-  const int qrow = q0 + wave * 32 + l32;  // the query of this lane's column
+  // (wave-uniform: read from the first lane, so that the head's pointers stay scalar)
+  const int hq = hk * a.G + it.sub * hp + ((hp == 2) ? (__builtin_amdgcn_readfirstlane(wave) / Ctx::HALF) : 0);
+  const int q0 = it.tile << lg_rows;
+  const int qrow = q0 + wr * 32 + l32;  // the query of this lane's column
   bind_seq(a, b);
   if (q0 >= a.Nq) return;  // past the end of a shorter packed sequence (whole workgroup)
 
@@ -321,10 +344,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Visible keys of this lane's query, and the workgroup's key tiles.
   x.lo_i = key_lo(a, qrow);
   x.hi_i = key_hi(a, qrow);
-  const int q_last = min(q0 + BM, a.Nq) - 1;
+  const int q_last = min(q0 + (1 << lg_rows), a.Nq) - 1;
   const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
   // Tiles that every query of this wave sees in full skip the element mask.
-  const int wq0 = q0 + 32 * __builtin_amdgcn_readfirstlane(wave);
+  const int wq0 = q0 + 32 * __builtin_amdgcn_readfirstlane(wr);
   x.lo_max = key_lo(a, min(wq0 + 31, a.Nq - 1));
   x.hi_min = key_hi(a, wq0);
   x.t_lo = kv_lo / BN;
@@ -443,8 +466,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <class T, int D, int BN, int NW>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int BM = NW * 32;
-  const int n_qt = (a.Nq + BM - 1) / BM;
-  const int64_t total = (int64_t)a.B * a.Hkv * n_qt * a.G;
+  const int hp = fwd_heads_per_workgroup(a);
+  const int n_qt = padded_tiles((a.Nq + BM / hp - 1) / (BM / hp), work_tiles_per_group(a, a.G / hp));
+  const int64_t total = (int64_t)a.B * a.Hkv * n_qt * (a.G / hp);
   if (total == 0) return hipSuccess;
   AttnArgs args = a;
   args.xcd_remap = a.xcd_remap && ((a.B * a.Hkv) % 8 == 0);
