@@ -108,11 +108,11 @@ def flops(w):
 # They describe the kernels built from the sources whose SHA-256 is recorded
 # here and are reported as null for any other source.
 COUNTERS = {
-    "sources_sha256": "afb71dcd7a1f3d973d8b8972eab8b3da477dd807a366ae94983b23496cf4e696",
-    "fwd_pp_kernel": {"mfma_busy": 0.673, "traffic": 572900000},
+    "sources_sha256": "205e3529300ca4066fa70d92771dbb74640fdb75ebdc05402ab5f4e7ed64bf2d",
+    "fwd_pp_kernel": {"mfma_busy": 0.669, "traffic": 572500000},
     "bwd_preprocess_kernel": {"mfma_busy": None, "traffic": 293700000},
-    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.514, "traffic": 1943100000},
-    "bwd_dq_kernel": {"mfma_busy": 0.688, "traffic": 709300000},
+    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.52, "traffic": 1939100000},
+    "bwd_dq_kernel": {"mfma_busy": 0.699, "traffic": 709300000},
 }
 
 def kernel_sources_sha():
