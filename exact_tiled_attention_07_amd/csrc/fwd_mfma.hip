@@ -123,23 +123,25 @@ struct FwdPP {
     return *reinterpret_cast<const u32x4*>(Ks + kb * 32 * 2 * D + kro[st]);
   }
 
-  // MFMA interval of tile m (relative to t_lo); PAR = m & 1.  Every interval
-  // runs both products: in interval 0 there is no tile -1, and P^T and the V
-  // buffer it reads start as zeros, so that product adds 0; after the last
-  // tile the S product reads a stale K buffer and its result is never used.
+  // MFMA interval of tile m (relative to t_lo); PAR = m & 1.  PV: run
+  // O += V(m-1)^T P(m-1)^T (false in interval 0, where there is no tile -1);
+  // SP: run S(m) = K(m) Q^T (false in interval n, after the last tile).  The
+  // skipped products would add zeros to O, or scores that are never used.
   // Each LDS operand is read NB - 1 MFMAs ahead of its use.
   // s[kb][r] is key j0 + 32*kb + 8*(r/4) + 4*hf + r%4.
-  template <int PAR>
+  template <int PAR, bool PV, bool SP>
   __device__ __forceinline__ void mfma_interval(int m, bool group_a) {
-    constexpr int NB = FA_FWD_RING, NO = NPV + NS;
-    static_assert(NPV >= NB, "interval shape");
+    constexpr int NB = FA_FWD_RING, O0 = PV ? 0 : NPV, O1 = SP ? NPV + NS : NPV;
+    static_assert(NPV >= NB && NS >= NB, "interval shape");
     const char* Vs = reinterpret_cast<const char*>(vbuf + (1 - PAR) * TILE);
     const char* Ks = reinterpret_cast<const char*>(kbuf + PAR * TILE);
+    if constexpr (SP) {
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
+      for (int kb = 0; kb < BN / 32; ++kb) s[kb] = f32x16{};
+    }
 #pragma unroll
-    for (int o = 0; o < NO; ++o) {
-      if (o + NB - 1 < NO) ring[(o + NB - 1) % NB] = operand(Vs, Ks, o + NB - 1);
+    for (int o = O0; o < O1; ++o) {
+      if (o + NB - 1 < O1) ring[(o + NB - 1) % NB] = operand(Vs, Ks, o + NB - 1);
       __builtin_amdgcn_sched_barrier(0);
       if (o < NPV) {
         const int si = o / (D / 32), db = o % (D / 32);
@@ -162,17 +164,17 @@ struct FwdPP {
     }
   }
 
-  // The first NB - 1 operands of the next MFMA interval (buffer parity PAR),
-  // read before the barrier that opens it, so that its first MFMA does not
-  // wait out an LDS round trip after the barrier.  They come from the V tile
-  // of that interval's P V product, which an earlier barrier published.
-  template <int PAR>
+  // The first NB - 1 operands of the next MFMA interval (buffer parity PAR;
+  // PV as in mfma_interval), read before the barrier that opens it, so that
+  // its first MFMA does not wait out an LDS round trip after the barrier.
+  // They come from tiles that an earlier barrier published.
+  template <int PAR, bool PV>
   __device__ __forceinline__ void prefetch() {
-    constexpr int NB = FA_FWD_RING;
+    constexpr int NB = FA_FWD_RING, O0 = PV ? 0 : NPV;
     const char* Vs = reinterpret_cast<const char*>(vbuf + (1 - PAR) * TILE);
     const char* Ks = reinterpret_cast<const char*>(kbuf + PAR * TILE);
 #pragma unroll
-    for (int o = 0; o < NB - 1; ++o) ring[o % NB] = operand(Vs, Ks, o);
+    for (int o = O0; o < O0 + NB - 1; ++o) ring[o % NB] = operand(Vs, Ks, o);
   }
 
   // Softmax interval of tile m: mask, row max, lazy rescale of O and l, P.
@@ -371,13 +373,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   x.l = 0.f;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) x.oacc[db] = f32x16{};
-#pragma unroll
-  for (int si = 0; si < BN / 16; ++si) x.pf[si] = u32x4{0u, 0u, 0u, 0u};
-  // V buffer 1 is first loaded for tile 1; interval 0's product reads it as zeros.
-  static_assert((TILE * 2) % (512 * 16) == 0, "V buffer clears in 16-byte stores");
-#pragma unroll
-  for (int i = 0; i < TILE * 2 / (512 * 16); ++i)
-    reinterpret_cast<u32x4*>(vbuf + TILE)[i * 512 + tid] = u32x4{0u, 0u, 0u, 0u};
 
   // Group A loads the K tiles, group B the V tiles; K(0) and V(0) here.
   x.kd.init(wave % Ctx::HALF, lane, a.k_sn, a.D / 8);
@@ -391,54 +386,87 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   __syncthreads();
 
-  // 2(n+1) intervals; both groups pass the same barriers.
+  // 2(n+1) intervals; both groups pass the same barriers.  Interval 0 runs
+  // only S(0) and interval n only the last P V product; m is odd in the tail.
   const int n = x.n;
-  int m = 0;
-  if (group_a) {
-    x.template prefetch<0>();
-    for (; m + 1 <= n; m += 2) {
-      x.template mfma_interval<0>(m, true);
+  if (n > 0) {
+    int m = 1;
+    if (group_a) {
+      x.template prefetch<0, false>();
+      x.template mfma_interval<0, false, true>(0, true);
       lds_barrier();
-      x.softmax_interval(m);
+      x.softmax_interval(0);
       wait_all_loads();
-      x.template prefetch<1>();
+      x.template prefetch<1, true>();
       lds_barrier();
-      x.template mfma_interval<1>(m + 1, true);
-      lds_barrier();
-      x.softmax_interval(m + 1);
+      for (; m + 1 < n; m += 2) {
+        x.template mfma_interval<1, true, true>(m, true);
+        lds_barrier();
+        x.softmax_interval(m);
+        wait_all_loads();
+        x.template prefetch<0, true>();
+        lds_barrier();
+        x.template mfma_interval<0, true, true>(m + 1, true);
+        lds_barrier();
+        x.softmax_interval(m + 1);
+        wait_all_loads();
+        x.template prefetch<1, true>();
+        lds_barrier();
+      }
+      if (m == n) {
+        x.template mfma_interval<1, true, false>(m, true);
+        lds_barrier();
+        wait_all_loads();
+        lds_barrier();
+      } else {
+        x.template mfma_interval<1, true, true>(m, true);
+        lds_barrier();
+        x.softmax_interval(m);
+        wait_all_loads();
+        x.template prefetch<0, true>();
+        lds_barrier();
+        x.template mfma_interval<0, true, false>(n, true);
+        lds_barrier();
+        wait_all_loads();
+        lds_barrier();
+      }
+    } else {
       wait_all_loads();
-      x.template prefetch<0>();
+      x.template prefetch<0, false>();
       lds_barrier();
-    }
-    if (m <= n) {
-      x.template mfma_interval<0>(m, true);
+      x.template mfma_interval<0, false, true>(0, false);
       lds_barrier();
-      x.softmax_interval(m);
-      wait_all_loads();
-      lds_barrier();
-    }
-  } else {
-    for (; m + 1 <= n; m += 2) {
+      for (; m + 1 < n; m += 2) {
+        x.softmax_interval(m - 1);
+        wait_all_loads();
+        x.template prefetch<1, true>();
+        lds_barrier();
+        x.template mfma_interval<1, true, true>(m, false);
+        lds_barrier();
+        x.softmax_interval(m);
+        wait_all_loads();
+        x.template prefetch<0, true>();
+        lds_barrier();
+        x.template mfma_interval<0, true, true>(m + 1, false);
+        lds_barrier();
+      }
       x.softmax_interval(m - 1);
       wait_all_loads();
-      x.template prefetch<0>();
+      x.template prefetch<1, true>();
       lds_barrier();
-      x.template mfma_interval<0>(m, false);
-      lds_barrier();
-      x.softmax_interval(m);
-      wait_all_loads();
-      x.template prefetch<1>();
-      lds_barrier();
-      x.template mfma_interval<1>(m + 1, false);
-      lds_barrier();
-    }
-    if (m <= n) {
-      x.softmax_interval(m - 1);
-      wait_all_loads();
-      x.template prefetch<0>();
-      lds_barrier();
-      x.template mfma_interval<0>(m, false);
-      lds_barrier();
+      if (m == n) {
+        x.template mfma_interval<1, true, false>(m, false);
+        lds_barrier();
+      } else {
+        x.template mfma_interval<1, true, true>(m, false);
+        lds_barrier();
+        x.softmax_interval(m);
+        wait_all_loads();
+        x.template prefetch<0, true>();
+        lds_barrier();
+        x.template mfma_interval<0, true, false>(n, false);
+        lds_barrier();
+      }
     }
   }
 
