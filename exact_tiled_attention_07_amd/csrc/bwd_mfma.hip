@@ -690,14 +690,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int tpg = work_tiles_per_group(a, a.G);
-  const int n_qt = padded_tiles((a.Nq + BM - 1) / BM, tpg);
+  // With an even GQA group, waves 0 .. NW/2 - 1 and NW/2 .. NW - 1 take the
+  // same 128 query rows of two query heads that share the K/V head, as in the
+  // forward, so that both halves end at the same causal key tile.
+  static_assert(BM == 256, "rows per head are 256 or 128");
+  const int hp = heads_per_workgroup(a);
+  const int lg_rows = (hp == 2) ? 7 : 8;  // query rows per head: BM / hp
+  const int wr = (hp == 2) ? (wave & (NW / 2 - 1)) : wave;
+  const int n_sub = a.G >> (hp - 1);
+  const int tpg = work_tiles_per_group(a, n_sub);
+  const int n_qt = padded_tiles((a.Nq + (1 << lg_rows) - 1) >> lg_rows, tpg);
   const bool heavy_last = (a.causal || a.wr >= 0) && a.wl < 0;
-  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_qt, a.G, heavy_last, a.xcd_remap, tpg);
+  const WorkItem it = decode_work(blockIdx.x, a.B * a.Hkv, n_qt, n_sub, heavy_last, a.xcd_remap, tpg);
   const int b = it.unit / a.Hkv, hk = it.unit % a.Hkv;
-  const int hq = hk * a.G + it.sub;
-  const int q0 = it.tile * BM;
-  const int qrow = q0 + wave * 32 + l32;
+  // (wave-uniform: read from the first lane, so that the head's pointers stay scalar)
+  const int hq = hk * a.G + it.sub * hp + ((hp == 2) ? (__builtin_amdgcn_readfirstlane(wave) / (NW / 2)) : 0);
+  const int q0 = it.tile << lg_rows;
+  const int qrow = q0 + wr * 32 + l32;
   bind_seq(a, b);
   if (q0 >= a.Nq) return;  // past the end of a shorter packed sequence (whole workgroup)
 
@@ -738,7 +747,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_DQ_W
 
   x.lo_i = key_lo(a, qrow);
   x.hi_i = key_hi(a, qrow);
-  const int q_last = min(q0 + BM, a.Nq) - 1;
+  const int q_last = min(q0 + (1 << lg_rows), a.Nq) - 1;
   const int kv_lo = key_lo(a, q0), kv_hi = key_hi(a, q_last);
   x.lo_max = key_lo(a, q_last);
   x.hi_min = key_hi(a, q0);
@@ -804,8 +813,10 @@ static hipError_t launch_bwd_t(const AttnArgs& a, hipStream_t stream, int stages
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int n_qt = padded_tiles((a.Nq + FA_DQ_NW * 32 - 1) / (FA_DQ_NW * 32), work_tiles_per_group(a, a.G));
-  const int64_t grid_q = (int64_t)a.B * a.Hkv * n_qt * a.G;
+  static_assert(FA_DQ_NW == 8, "the dQ kernel pairs query heads over its two halves of 4 waves");
+  const int hp = heads_per_workgroup(a), rows = FA_DQ_NW * 32 / hp;
+  const int n_qt = padded_tiles((a.Nq + rows - 1) / rows, work_tiles_per_group(a, a.G / hp));
+  const int64_t grid_q = (int64_t)a.B * a.Hkv * n_qt * (a.G / hp);
   if (grid_q > 0 && (stages & kStageDq)) {
     if (a.mod)
       // 32-key tiles at d = 128: the modifiers' per-element work does not fit

@@ -50,18 +50,6 @@ static constexpr float kLazyBound = 256.0f - 0.25f;
 #define FA_FWD_RING 3  // LDS operands in flight ahead of the MFMA that uses them
 #endif
 
-// Query heads per workgroup.  The 256 query rows of a workgroup are either
-// 256 rows of one query head or, when the GQA group size is even, the same 128
-// rows of two query heads that read the same K/V head (wave group A one head,
-// group B the other).  Under a causal mask a workgroup's key range then ends
-// where its last query row's does for both groups, instead of two 64-key
-// tiles later than group A needs (forward 1.4-1.9% faster at N = 8192, 13%
-// at N = 512, batch 8).  A packed batch pairs heads only when the group size is a
-// multiple of 4, so that each (unit, tile) keeps an even number of workgroups
-// (decode_work: with one per (unit, tile) a packed batch of G = 2 ran 5% slower).
-__host__ __device__ __forceinline__ int fwd_heads_per_workgroup(const AttnArgs& a) {
-  return (a.G % (a.cu_q ? 4 : 2) == 0) ? 2 : 1;
-}
 
 // ---------------------------------------------------------------------------
 // Forward with two wave groups in ping-pong.
@@ -295,8 +283,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bool group_a = wave < Ctx::HALF;
 
   // With an even GQA group the two wave groups take the same 128 query rows
-  // of two query heads that share the K/V head (fwd_heads_per_workgroup).
-  const int hp = fwd_heads_per_workgroup(a);
+  // of two query heads that share the K/V head (heads_per_workgroup).
+  const int hp = heads_per_workgroup(a);
   const int lg_rows = (hp == 2) ? 7 : 8;                 // query rows per head: BM / hp
   static_assert(BM == 256, "rows per head are 256 or 128");
   const int wr = (hp == 2) ? (wave & (Ctx::HALF - 1)) : wave;  // row block of this wave
@@ -494,7 +482,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <class T, int D, int BN, int NW>
 static hipError_t launch_fwd_t(const AttnArgs& a, hipStream_t stream) {
   constexpr int BM = NW * 32;
-  const int hp = fwd_heads_per_workgroup(a);
+  const int hp = heads_per_workgroup(a);
   const int n_qt = padded_tiles((a.Nq + BM / hp - 1) / (BM / hp), work_tiles_per_group(a, a.G / hp));
   const int64_t total = (int64_t)a.B * a.Hkv * n_qt * (a.G / hp);
   if (total == 0) return hipSuccess;
