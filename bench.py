@@ -108,11 +108,11 @@ def flops(w):
 # They describe the kernels built from the sources whose SHA-256 is recorded
 # here and are reported as null for any other source.
 COUNTERS = {
-    "sources_sha256": "205e3529300ca4066fa70d92771dbb74640fdb75ebdc05402ab5f4e7ed64bf2d",
-    "fwd_pp_kernel": {"mfma_busy": 0.669, "traffic": 572500000},
+    "sources_sha256": "0d50ff92d63819c9f237bd37357d377fa9c3f189ae41bd1b2a4bc7a8c60dad39",
+    "fwd_pp_kernel": {"mfma_busy": 0.669, "traffic": 571300000},
     "bwd_preprocess_kernel": {"mfma_busy": None, "traffic": 293700000},
-    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.52, "traffic": 1939100000},
-    "bwd_dq_kernel": {"mfma_busy": 0.699, "traffic": 709300000},
+    "bwd_dkdv_ws_kernel": {"mfma_busy": 0.52, "traffic": 1927700000},
+    "bwd_dq_kernel": {"mfma_busy": 0.69, "traffic": 707400000},
 }
 
 def kernel_sources_sha():
